@@ -1,0 +1,325 @@
+// Split-context decode attention and its cross-partition log-sum-exp reduce.
+//
+// What is computed ("vLLM 学习笔记 01", sections 1.4-1.6): a decode segment
+// has one new token at position L-1 of a sequence whose L keys/values sit in
+// 16-token blocks listed by the segment's block table; its query heads of
+// group g (G = Hq/Hkv of them) attend to all L keys of KV head g.  Decode
+// reads every cached K/V byte once per step, so it is bound by HBM bandwidth
+// ("从0开始的vLLM学习": decode is memory-bandwidth bound).
+//
+// Work split: a work item is (segment, partition of P keys, KV head) and is
+// run by one wavefront; partitions of long contexts run on different waves
+// and are merged by decode_reduce_kernel with the online-softmax identity
+// (each partition keeps its running max m, sum l and unnormalised output o;
+// the merge rescales by exp(m_p - max_p m_p)).
+//
+// Per wave, per 32 keys (two blocks):
+//   S^T[key, head] = K[key, :] . Q[head, :]     16x16x32 bf16 MFMA, D/32 slabs,
+//                                               Q (zero-padded to 16 heads) in
+//                                               registers for the whole item
+//   online softmax in fp32 (exp2 with scale*log2(e) folded in)
+//   O^T[d, head] += V^T[d, key] . P^T[key, head] 16x16x32 bf16 MFMA, D/16 tiles
+// The C layout of the first product (lane = head, 4 keys per lane group) is
+// exactly the B operand layout the second product needs, so P never leaves
+// its registers.  V rows are loaded fully coalesced (16 lanes cover one
+// 256-byte row) with a permuted d order (tile t, row m <-> d = (D/16)*m + t)
+// and transposed to the A operand with v_perm in registers.  Next 32 keys'
+// K/V loads are issued before the current 32 keys are computed.
+#include "kernels.hpp"
+
+namespace pkv {
+
+template <int D>
+struct KvRegs {
+  static constexpr int NS = D / 32;           // 32-wide d slabs of the QK product
+  static constexpr int VW = D / 32;           // dwords of one lane's V piece (D/16 bf16)
+  u32x4 k[2][NS];
+  uint32_t v[8][VW];
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv(KvRegs<D>& r, const uint16_t* __restrict__ cache,
+                                        int64_t off0, int64_t off1, bool ok0, bool ok1,
+                                        int kb, int key1, int m, int j, int64_t row_elems) {
+  constexpr int NS = KvRegs<D>::NS;
+  constexpr int VW = KvRegs<D>::VW;
+  constexpr int NT = D / 16;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t off = b ? off1 : off0;
+    const bool okb = b ? ok1 : ok0;
+    const bool kval = okb && (kb + 16 * b + m < key1);
+    const uint16_t* kp = cache + off + m * row_elems + 8 * j;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      r.k[b][sl] = kval ? *reinterpret_cast<const u32x4*>(kp + 32 * sl) : z;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = i >> 2;
+    const int row = 4 * j + (i & 3);
+    const int64_t off = b ? off1 : off0;
+    const bool okb = b ? ok1 : ok0;
+    const bool vval = okb && (kb + 16 * b + row < key1);
+    const uint16_t* vp = cache + off + (int64_t)(kBlock + row) * row_elems + NT * m;
+    if constexpr (VW == 4) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      u32x4 x = vval ? *reinterpret_cast<const u32x4*>(vp) : z;
+      r.v[i][0] = x[0]; r.v[i][1] = x[1]; r.v[i][2] = x[2]; r.v[i][3] = x[3];
+    } else {
+      u32x2 z = {0u, 0u};
+      u32x2 x = vval ? *reinterpret_cast<const u32x2*>(vp) : z;
+      r.v[i][0] = x[0]; r.v[i][1] = x[1];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf)[D / 32],
+                                            f32x4 (&o)[D / 16], float& m_run, float& l_run,
+                                            int kb, int key1, bool ok0, bool ok1, int j,
+                                            float scale_log2) {
+  constexpr int NS = D / 32;
+  constexpr int NT = D / 16;
+  f32x4 sc[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) sc[b] = mfma16(r.k[b][sl], qf[sl], sc[b]);
+  }
+  float x[8];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = i >> 2;
+    const bool okb = b ? ok1 : ok0;
+    const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < key1);
+    x[i] = live ? sc[b][i & 3] * scale_log2 : -INFINITY;
+    cmax = fmaxf(cmax, x[i]);
+  }
+  cmax = wave_max_xor(cmax, 16);
+  cmax = wave_max_xor(cmax, 32);
+  const float m_new = fmaxf(m_run, cmax);
+  // all keys so far left out (only for blocks skipped as invalid): keep state
+  const bool none = m_new == -INFINITY;
+  const float alpha = none ? 1.f : exp2f(m_run - m_new);
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = none ? 0.f : exp2f(x[i] - m_new);
+    psum += p[i];
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  u32x4 pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+              pack_bf16(p[6], p[7])};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    o[t] *= alpha;
+    const int w = t >> 1;
+    const bool hi = t & 1;
+    u32x4 a = {pick_halves(r.v[0][w], r.v[1][w], hi), pick_halves(r.v[2][w], r.v[3][w], hi),
+               pick_halves(r.v[4][w], r.v[5][w], hi), pick_halves(r.v[6][w], r.v[7][w], hi)};
+    o[t] = mfma16(a, pb, o[t]);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_kernel(DecodeParams p) {
+  constexpr int NS = D / 32;
+  constexpr int NT = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15;
+  const int j = lane >> 4;
+  const int n_items = p.hdr->n_decode * p.hkv;
+  const int64_t row_elems = (int64_t)p.hkv * D;
+  const int64_t block_elems = 2 * kBlock * row_elems;
+
+  for (;;) {
+    int it = 0;
+    if (lane == 0) it = atomicAdd(&p.hdr->decode_next, 1);
+    it = wave_uniform(__shfl(it, 0));
+    if (it >= n_items) break;
+    const int2 item = p.items[it / p.hkv];
+    const int g = it % p.hkv;
+    const int s = item.x;
+    const int part = item.y;
+    const int L = p.lens[s];
+    const int tok = p.cu[s];
+    const int key0 = part * p.part_tokens;
+    const int key1 = min(L, key0 + p.part_tokens);
+    const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+
+    const bool head_live = m < p.group;
+    u32x4 qf[NS];
+    {
+      const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride + (int64_t)(g * p.group + m) * D + 8 * j;
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qf[sl] = head_live ? *reinterpret_cast<const u32x4*>(qrow + 32 * sl) : z;
+      }
+    }
+    // the partition's block ids, one per lane (P <= 1024 keys = 64 blocks)
+    const int nblk = (key1 - key0 + kBlock - 1) / kBlock;
+    int my_bid = -1;
+    if (lane < nblk) my_bid = p.bt[(int64_t)s * p.width + key0 / kBlock + lane];
+    const bool bad_bid = lane < nblk && (my_bid < 0 || (int64_t)my_bid >= p.num_blocks);
+    if (__any(bad_bid)) {
+      if (lane == 0) atomicOr(&p.hdr->status, 2u);
+    }
+
+    f32x4 o[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    auto block_at = [&](int kb, int b, int64_t& off, bool& ok) {
+      const int blk = (kb - key0) / kBlock + b;
+      const bool exists = kb + kBlock * b < key1;
+      const int bid = exists ? __builtin_amdgcn_readlane(my_bid, blk) : -1;
+      ok = exists && bid >= 0 && (int64_t)bid < p.num_blocks;
+      off = ok ? (int64_t)bid * block_elems + (int64_t)g * D : 0;
+    };
+
+    KvRegs<D> ra, rb;
+    int64_t a0, a1, b0, b1;
+    bool ao0, ao1, bo0, bo1;
+    block_at(key0, 0, a0, ao0);
+    block_at(key0, 1, a1, ao1);
+    load_kv<D>(ra, p.cache, a0, a1, ao0, ao1, key0, key1, m, j, row_elems);
+    for (int kb = key0; kb < key1; kb += 64) {
+      const int kn = kb + 32;
+      if (kn < key1) {
+        block_at(kn, 0, b0, bo0);
+        block_at(kn, 1, b1, bo1);
+        load_kv<D>(rb, p.cache, b0, b1, bo0, bo1, kn, key1, m, j, row_elems);
+      }
+      attend_step<D>(ra, qf, o, m_run, l_run, kb, key1, ao0, ao1, j, p.scale_log2);
+      if (kn >= key1) break;
+      const int kn2 = kb + 64;
+      if (kn2 < key1) {
+        block_at(kn2, 0, a0, ao0);
+        block_at(kn2, 1, a1, ao1);
+        load_kv<D>(ra, p.cache, a0, a1, ao0, ao1, kn2, key1, m, j, row_elems);
+      }
+      attend_step<D>(rb, qf, o, m_run, l_run, kn, key1, bo0, bo1, j, p.scale_log2);
+    }
+
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (head_live) {
+      const int hq = g * p.group + m;
+      if (nparts == 1) {
+        const float inv = 1.f / l_run;
+        uint16_t* orow = p.out + ((int64_t)tok * p.hq + hq) * D;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          uint32_t wv[NT / 2];
+#pragma unroll
+          for (int t = 0; t < NT; t += 2) wv[t / 2] = pack_bf16(o[t][rr] * inv, o[t + 1][rr] * inv);
+          uint16_t* dst = orow + NT * (4 * j + rr);
+          if constexpr (NT == 8) {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+          } else {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
+          }
+        }
+      } else {
+        const int64_t slot = ((int64_t)s * p.pmax + part) * p.hq + hq;
+        float* prow = p.part_o + slot * D;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          float* dst = prow + NT * (4 * j + rr);
+#pragma unroll
+          for (int t = 0; t < NT; t += 4)
+            *reinterpret_cast<f32x4*>(dst + t) = f32x4{o[t][rr], o[t + 1][rr], o[t + 2][rr], o[t + 3][rr]};
+        }
+        if (j == 0) p.part_ml[slot] = make_float2(m_run, l_run);
+      }
+    }
+  }
+}
+
+// Merge of the partitions of every multi-partition decode segment.  One wave
+// per (segment, query head); lanes split d.  The weights exp2(m_p - max m)
+// rescale each partition's sum and output to the common maximum.
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int hchunks = (p.hq + 3) / 4;
+  const int s = blockIdx.x / hchunks;
+  const int hq = (blockIdx.x % hchunks) * 4 + (threadIdx.x >> 6);
+  if (s >= num_seqs || hq >= p.hq) return;
+  const int c0 = p.cu[s];
+  const int c1 = p.cu[s + 1];
+  const int L = p.lens[s];
+  if (c0 < 0 || c1 > num_tokens || c1 - c0 != 1 || L < 1 || L > p.width * kBlock) return;
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  if (nparts <= 1) return;
+  const int64_t base = (int64_t)s * p.pmax * p.hq + hq;   // slot of partition 0
+  float mx = -INFINITY;
+  for (int i = lane; i < nparts; i += 64) mx = fmaxf(mx, p.part_ml[base + (int64_t)i * p.hq].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float den = 0.f;
+  for (int i = lane; i < nparts; i += 64) {
+    const float2 ml = p.part_ml[base + (int64_t)i * p.hq];
+    den += ml.x == -INFINITY ? 0.f : ml.y * exp2f(ml.x - mx);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int i = 0; i < nparts; ++i) {
+    const int64_t slot = base + (int64_t)i * p.hq;
+    const float mp = p.part_ml[slot].x;
+    const float w = mp == -INFINITY ? 0.f : exp2f(mp - mx);
+    const float* src = p.part_o + slot * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w * src[e];
+  }
+  const float inv = 1.f / den;
+  uint16_t* dst = p.out + ((int64_t)c0 * p.hq + hq) * D + lane * PER;
+  if constexpr (PER == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
+  } else {
+    __bf16 b = (__bf16)(acc[0] * inv);
+    *dst = __builtin_bit_cast(uint16_t, b);
+  }
+}
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, int num_seqs,
+                         int num_tokens, hipStream_t stream) {
+  if (head_dim == 128) {
+    decode_kernel<128><<<grid, 256, 0, stream>>>(p);
+  } else {
+    decode_kernel<64><<<grid, 256, 0, stream>>>(p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int hchunks = (p.hq + 3) / 4;
+  const int rgrid = num_seqs * hchunks;
+  if (rgrid == 0) return hipSuccess;
+  if (head_dim == 128) {
+    decode_reduce_kernel<128><<<rgrid, 256, 0, stream>>>(p, num_seqs, num_tokens);
+  } else {
+    decode_reduce_kernel<64><<<rgrid, 256, 0, stream>>>(p, num_seqs, num_tokens);
+  }
+  return hipGetLastError();
+}
+
+const void* decode_kernel_ptr(int head_dim) {
+  return head_dim == 128 ? (const void*)decode_kernel<128> : (const void*)decode_kernel<64>;
+}
+
+}  // namespace pkv

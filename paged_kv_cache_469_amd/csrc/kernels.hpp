@@ -1,0 +1,73 @@
+// Kernel parameter blocks and launchers shared by the kernel sources and the
+// host-side C ABI layer.
+#pragma once
+
+#include "common.hpp"
+
+namespace pkv {
+
+struct PlanParams {
+  const int32_t* cu;
+  const int32_t* lens;
+  WsHeader* hdr;
+  int2* decode_items;
+  int2* prefill_items;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t max_len;       // max_blocks_per_seq * 16
+  int32_t part_tokens;   // P
+  int32_t query_tile;    // QT
+  int32_t decode_cap;    // capacity of decode_items
+  int32_t prefill_cap;   // capacity of prefill_items
+};
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint16_t* cache;
+  const int32_t* bt;
+  const int32_t* cu;
+  const int32_t* lens;
+  uint16_t* out;
+  float* part_o;           // [S, pmax, Hq, D]
+  float2* part_ml;         // [S, pmax, Hq]  (running max in log2 units, sum)
+  WsHeader* hdr;
+  const int2* items;       // (segment, partition)
+  int64_t q_stride;
+  int64_t num_blocks;
+  int32_t width;           // block table row length
+  int32_t hq, hkv, group;
+  int32_t part_tokens;     // P, a multiple of 32, <= 1024
+  int32_t pmax;
+  float scale_log2;        // scale * log2(e)
+};
+
+struct PrefillParams {
+  const uint16_t* q;
+  const uint16_t* cache;
+  const int32_t* bt;
+  const int32_t* cu;
+  const int32_t* lens;
+  uint16_t* out;
+  WsHeader* hdr;
+  const int2* items;       // (segment, query tile)
+  int64_t q_stride;
+  int64_t num_blocks;
+  int32_t width;
+  int32_t hq, hkv, group;
+  int32_t heads_per_item;  // HW: heads handled by one work item (1, 2 or 4)
+  int32_t head_chunks;     // group / HW
+  float scale_log2;
+};
+
+hipError_t launch_kv_write(const void* k, const void* v, const int32_t* slots, void* cache,
+                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           int64_t num_blocks, int64_t k_stride, int64_t v_stride,
+                           hipStream_t stream);
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, int num_seqs,
+                         int num_tokens, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int grid, hipStream_t stream);
+const void* decode_kernel_ptr(int head_dim);
+const void* prefill_kernel_ptr(int head_dim);
+
+}  // namespace pkv

@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+KV writes are compared bit for bit with the oracle's write of the same
+inputs; attention element by element within 2e-2 + 1e-2*|ref| plus the
+relative-RMS gate (see gpu_harness).  Sizes: every workload at a reduced
+size the oracle finishes in seconds (all rows checked, several tiles and
+partitions, ragged tails), and at full size with sampled segments and rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_469_amd as pkv
+import workloads
+from gpu_harness import DeviceStep, check_close, down_u16, log, oracle_rows, up
+from oracle import bf16, paged
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = [
+    ("tiny_mixed", {}),
+    ("decode_8b", dict(num_requests=24)),
+    ("prefill_8b", dict(num_prompts=4, lens=(200, 700))),
+    ("cb_step_8b", dict(num_decodes=12, ctx=(1024, 3000), shared=4, prefix=1024, chunk=300,
+                        chunk_history=700)),
+    ("cb_step_8b", dict(num_decodes=12, ctx=(1024, 3000), shared=4, prefix=1024, chunk=300,
+                        chunk_history=700, decode_first=False)),
+    ("long_decode_70b", dict(num_requests=3, ctx=(4000, 20000))),
+]
+
+
+@pytest.mark.parametrize("name,kw", REDUCED, ids=[f"{n}-{i}" for i, (n, _) in enumerate(REDUCED)])
+def test_reduced_full_check(name, kw):
+    wl = workloads.make(name, **kw)
+    log(f"case {name} {kw}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")
+    st = DeviceStep(wl, host_pool=True)
+    out = st.attend()
+    assert np.array_equal(down_u16(st.pool), st.host), "KV pool differs from the oracle's write"
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens,
+                       wl.scale)
+    check_close(down_u16(out), ref, name)
+    assert st.status() == 0
+
+
+@pytest.mark.parametrize("name,kw", REDUCED[1:4], ids=["decode", "prefill", "cb"])
+def test_sharpened_queries(name, kw):
+    # q x 4: logits with std 4, outputs O(0.1-1); correctness only
+    wl = workloads.make(name, **kw)
+    log(f"case sharpened {name}")
+    st = DeviceStep(wl, q_gain=4.0)
+    out = down_u16(st.attend())
+    refs = oracle_rows(wl, st.q_host)
+    rows = np.concatenate([r for r, _ in refs.values()])
+    ref = np.concatenate([x for _, x in refs.values()])
+    check_close(out[rows], ref, f"sharpened {name}")
+
+
+def _custom(hq, hkv, d, segs, cfg=50, **kw):
+    return workloads.build("custom", cfg, hq, hkv, d, segs, **kw)
+
+
+EDGE = [
+    ("mha_d64", dict(hq=8, hkv=8, d=64, segs=[(1, 1), (1, 16), (1, 17), (5, 5), (0, 9), (33, 80)])),
+    ("g2_d128", dict(hq=16, hkv=8, d=128, segs=[(2, 2), (1, 1024), (1, 1025), (64, 64), (3, 700)])),
+    ("g3_d128", dict(hq=6, hkv=2, d=128, segs=[(1, 300), (17, 17), (100, 260)])),
+    ("g8_d64", dict(hq=32, hkv=4, d=64, segs=[(6, 6), (1, 38), (40, 40), (1, 2049)])),
+    ("g16_d128", dict(hq=32, hkv=2, d=128, segs=[(1, 513), (70, 100)])),
+    ("zero_len_segments", dict(hq=32, hkv=8, d=128, segs=[(0, 0), (1, 33), (0, 40), (7, 7)])),
+    ("block_multiples", dict(hq=32, hkv=8, d=128, segs=[(1, 16), (1, 32), (1, 1024), (16, 16), (64, 128)])),
+]
+
+
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(name, kw):
+    wl = _custom(kw["hq"], kw["hkv"], kw["d"], kw["segs"], num_blocks=None)
+    log(f"case edge {name}")
+    st = DeviceStep(wl, host_pool=True)
+    sentinel = torch.full((wl.num_tokens, wl.num_q_heads, wl.head_dim), 7.0,
+                          dtype=torch.bfloat16, device="cuda")
+    out = down_u16(st.attend(out=sentinel))
+    assert np.array_equal(down_u16(st.pool), st.host)
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens,
+                       wl.scale)
+    check_close(out, ref, name)
+
+
+@pytest.mark.parametrize("tokens", [32, 64, 256, 1024])
+def test_partition_sizes(tokens):
+    wl = workloads.make("long_decode_70b", num_requests=3, ctx=(3000, 9000))
+    log(f"case partition {tokens}")
+    pkv.paged_attention_set_partition_tokens(tokens)
+    try:
+        st = DeviceStep(wl)
+        out = down_u16(st.attend())
+    finally:
+        pkv.paged_attention_set_partition_tokens(0)
+    refs = oracle_rows(wl, st.q_host)
+    rows = np.concatenate([r for r, _ in refs.values()])
+    check_close(out[rows], np.concatenate([x for _, x in refs.values()]), f"P={tokens}")
+
+
+def test_permutation_invariance_and_determinism():
+    kw = dict(num_decodes=10, ctx=(1024, 2500), shared=3, prefix=1024, chunk=130, chunk_history=300)
+    a = workloads.make("cb_step_8b", **kw)
+    b = workloads.make("cb_step_8b", num_blocks=a.num_blocks * 3, **kw)   # other placement
+    log("case permutation/determinism")
+    sa, sb = DeviceStep(a), DeviceStep(b)
+    oa1 = down_u16(sa.attend())
+    oa2 = down_u16(sa.attend())
+    ob = down_u16(sb.attend())
+    assert np.array_equal(oa1, oa2), "repeat run is not bitwise identical"
+    same = np.array_equal(oa1, ob)
+    log(f"  permuted pool bitwise identical: {same}")
+    refs = oracle_rows(b, sb.q_host)
+    rows = np.concatenate([r for r, _ in refs.values()])
+    check_close(ob[rows], np.concatenate([x for _, x in refs.values()]), "permuted")
+
+
+def test_write_strided_and_unaligned():
+    rng = np.random.default_rng(3)
+    t, hkv, d, nb = 37, 8, 128, 20
+    slots = rng.choice(nb * 16, size=t, replace=False).astype(np.int32)
+    slots[[2, 9]] = -1
+    host = np.full((nb, 2, 16, hkv, d), 0x7FC1, dtype=np.uint16)
+    for width in (hkv * d * 3, hkv * d + 4):    # 16-byte aligned stride, then not
+        log(f"case write stride {width}")
+        buf = rng.integers(0, 1 << 16, (t, width)).astype(np.uint16)
+        dev = up(buf)
+        k = dev[:, :hkv * d].view(t, hkv, d)
+        v = dev[:, width - hkv * d:].view(t, hkv, d)
+        pool = torch.empty((nb, 2, 16, hkv, d), dtype=torch.bfloat16, device="cuda")
+        pool.view(torch.int16).fill_(0x7FC1)
+        pkv.paged_kv_write(k, v, up(slots), pool)
+        torch.cuda.synchronize()
+        want = host.copy()
+        paged.kv_write(buf[:, :hkv * d].reshape(t, hkv, d), buf[:, width - hkv * d:].reshape(t, hkv, d),
+                       slots, want)
+        assert np.array_equal(down_u16(pool), want)
+
+
+def test_bad_metadata_is_skipped_and_flagged():
+    wl = _custom(32, 8, 128, [(1, 100), (1, 200), (4, 50)], cfg=51)
+    log("case bad metadata")
+    st = DeviceStep(wl)
+    good = down_u16(st.attend())
+    bt = wl.block_tables.copy()
+    bt[1, 3] = wl.num_blocks + 1000                      # outside the pool
+    st.bt = up(bt)
+    out = down_u16(st.attend())
+    assert st.status() & pkv.STATUS_BAD_BLOCK
+    assert np.array_equal(out[0], good[0]) and np.array_equal(out[2:], good[2:])
+    st.bt = up(wl.block_tables)
+    lens = wl.seq_lens.copy()
+    lens[0] = wl.max_blocks_per_seq * 16 + 5             # longer than its table
+    st.lens = up(lens)
+    out = down_u16(st.attend())
+    assert st.status() & pkv.STATUS_BAD_SEGMENT
+    assert np.array_equal(out[1:], good[1:])
+    with pytest.raises(pkv.PagedError):
+        pkv.paged_validate(None, st.bt, st.cu, st.lens, wl.num_tokens, wl.num_blocks)
+    st.lens = up(wl.seq_lens)
+    pkv.paged_validate(st.slots, st.bt, st.cu, st.lens, wl.num_tokens, wl.num_blocks)
+    dup = up(np.array([5, 5], dtype=np.int32))
+    with pytest.raises(pkv.PagedError, match="twice"):
+        pkv.paged_validate(dup, None, None, None, 0, wl.num_blocks)
+
+
+# ------------------------------------------------------------------ full size
+
+def _full_sampled(wl, sample_segments, rows_per_segment=None, pool_blocks=None, fill_others=False):
+    """Full-size workload.  Each request's K/V is written with one
+    paged_kv_write call over all its positions (the step's write order is
+    covered by the reduced cases).  With ``fill_others`` only the sampled
+    segments' values come from the host generator; the others are drawn on
+    the GPU (seeded) and are not compared."""
+    torch.cuda.empty_cache()
+    hkv, d = wl.num_kv_heads, wl.head_dim
+    nb = wl.num_blocks if pool_blocks is None else pool_blocks
+    pool = torch.empty((nb, 2, 16, hkv, d), dtype=torch.bfloat16, device="cuda")
+    pool.view(torch.int16).fill_(0x7FC1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(469)
+    sample = set(int(s) for s in sample_segments)
+    for s in range(wl.num_seqs):
+        length = int(wl.seq_lens[s])
+        slots = up(wl.slots_of(s, 0, length))
+        if s in sample or not fill_others:
+            k, v = wl.request_kv(s)
+            pkv.paged_kv_write(up(k), up(v), slots, pool)
+        else:
+            kv = torch.randn((2, length, hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+            pkv.paged_kv_write(kv[0], kv[1], slots, pool)
+            del kv
+    q_host = wl.q()
+    ws = torch.empty(pkv.paged_attention_workspace_size(
+        wl.num_seqs, wl.num_tokens, wl.num_q_heads, hkv, d, wl.max_blocks_per_seq),
+        dtype=torch.uint8, device="cuda")
+    out = pkv.paged_attention(up(q_host), pool, up(wl.block_tables), up(wl.cu_seqlens_q),
+                              up(wl.seq_lens), wl.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert pkv.paged_attention_device_status(ws) == 0
+    # write check on the sampled requests: their blocks hold exactly their K/V
+    for s in sample:
+        length = int(wl.seq_lens[s])
+        ids = torch.from_numpy(wl.block_tables[s][:(length + 15) // 16].astype(np.int64)).cuda()
+        blocks = pool.index_select(0, ids)
+        got = blocks.view(torch.int16).cpu().numpy().view(np.uint16)
+        gk = got[:, 0].reshape(-1, hkv, d)[:length]
+        gv = got[:, 1].reshape(-1, hkv, d)[:length]
+        rk, rv = wl.request_kv(s)
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv), f"segment {s} blocks"
+    refs = oracle_rows(wl, q_host, segments=sorted(sample), rows_per_segment=rows_per_segment,
+                       rng=np.random.default_rng(1))
+    got = down_u16(out)
+    rows = np.concatenate([r for r, _ in refs.values()])
+    ref = np.concatenate([x for _, x in refs.values()])
+    return got[rows], ref
+
+
+def test_full_decode_8b():
+    wl = workloads.make("decode_8b")
+    log(f"case full decode_8b: KV {wl.kv_bytes_logical() / 1e9:.2f} GB")
+    sample = np.random.default_rng(2).choice(wl.num_seqs, 12, replace=False)
+    got, ref = _full_sampled(wl, sample)
+    check_close(got, ref, "decode_8b full (12 sampled requests)")
+
+
+def test_full_prefill_8b():
+    wl = workloads.make("prefill_8b")
+    log(f"case full prefill_8b: T={wl.num_tokens}")
+    got, ref = _full_sampled(wl, [0, 5, 9, 15], rows_per_segment=24)
+    check_close(got, ref, "prefill_8b full (4 segments x 26 rows)")
+
+
+def test_full_cb_step_8b():
+    wl = workloads.make("cb_step_8b")
+    log(f"case full cb_step_8b: T={wl.num_tokens}")
+    chunk = wl.num_seqs - 1
+    got, ref = _full_sampled(wl, [0, 1, 63, 64, 150, chunk], rows_per_segment=24)
+    check_close(got, ref, "cb_step_8b full (5 decodes + 26 chunk rows)")
+
+
+def test_full_long_decode_70b():
+    free, _ = torch.cuda.mem_get_info()
+    nb = int(0.92 * (free - (4 << 30)) // 65536)
+    wl = workloads.make("long_decode_70b", num_blocks=nb)
+    log(f"case full long_decode_70b: pool {nb} blocks ({nb * 16} tokens), "
+        f"KV {wl.kv_bytes_logical() / 1e9:.1f} GB")
+    got, ref = _full_sampled(wl, [3, 40], pool_blocks=nb, fill_others=True)
+    check_close(got, ref, "long_decode_70b full (2 sampled requests)")
