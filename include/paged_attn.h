@@ -143,6 +143,15 @@ int paged_attention_device_status(const void* workspace, uint32_t* status,
  * Process-wide; returns PAGED_EINVAL for other values. */
 int paged_attention_set_partition_tokens(int32_t tokens);
 
+/* Measurement hook: when `count` is 5, every later paged_attention call on
+ * this thread records events[0] before its first kernel and events[1..4]
+ * after the plan, decode, decode-merge and prefill kernels, on the call's
+ * stream, so a caller can read each stage's duration with
+ * hipEventElapsedTime.  The handles are hipEvent_t values created by the
+ * caller, who keeps them alive while calls use them.  count = 0 (or events =
+ * NULL) switches it off.  Returns PAGED_EINVAL for other counts. */
+int paged_attention_set_stage_events(void* const* events, int32_t count);
+
 const char* paged_last_error(void);
 
 #ifdef __cplusplus

@@ -29,6 +29,7 @@ _SIGS = {
                                 _c_i32, _c_p]),
     "paged_attention_device_status": (_c_i32, [_c_p, ctypes.POINTER(ctypes.c_uint32), _c_p]),
     "paged_attention_set_partition_tokens": (_c_i32, [_c_i32]),
+    "paged_attention_set_stage_events": (_c_i32, [ctypes.POINTER(_c_p), _c_i32]),
     "paged_last_error": (ctypes.c_char_p, []),
 }
 
@@ -183,3 +184,18 @@ def paged_attention_device_status(workspace, stream=None):
 
 def paged_attention_set_partition_tokens(tokens):
     _check(lib().paged_attention_set_partition_tokens(int(tokens)))
+
+
+def paged_attention_set_stage_events(events):
+    """Record the given 5 torch.cuda.Events around the stages of later
+    paged_attention calls on this thread (None switches it off)."""
+    if events is None:
+        _check(lib().paged_attention_set_stage_events(None, 0))
+        return
+    handles = []
+    for e in events:
+        if e.cuda_event == 0:          # torch creates the HIP event on first record
+            e.record()
+        handles.append(e.cuda_event)
+    arr = (_c_p * len(handles))(*handles)
+    _check(lib().paged_attention_set_stage_events(arr, len(handles)))

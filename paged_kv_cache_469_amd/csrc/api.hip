@@ -21,6 +21,12 @@ using namespace pkv;
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_stage_events[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_stage_on = false;
+
+hipError_t stage(int i, hipStream_t stream) {
+  return g_stage_on ? hipEventRecord(g_stage_events[i], stream) : hipSuccess;
+}
 std::atomic<int32_t> g_part_tokens{0};
 
 int fail(int code, const char* fmt, ...) {
@@ -231,7 +237,9 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   pp.query_tile = query_tile;
   pp.decode_cap = (int32_t)l.decode_cap;
   pp.prefill_cap = (int32_t)l.prefill_cap;
-  e = launch_plan(pp, stream);
+  e = stage(0, stream);
+  if (e == hipSuccess) e = launch_plan(pp, stream);
+  if (e == hipSuccess) e = stage(1, stream);
   if (e != hipSuccess) return fail_hip(e, "paged_attention plan launch");
 
   const int di = head_dim == 128 ? 1 : 0;
@@ -258,7 +266,10 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   const int64_t decode_waves = l.decode_cap * num_kv_heads;
   const int decode_grid = (int)std::max<int64_t>(
       1, std::min<int64_t>((int64_t)dev.cus * dev.decode_wg[di], (decode_waves + 3) / 4));
-  e = launch_decode(dp, head_dim, decode_grid, num_seqs, num_tokens, stream);
+  e = launch_decode(dp, head_dim, decode_grid, stream);
+  if (e == hipSuccess) e = stage(2, stream);
+  if (e == hipSuccess) e = launch_decode_merge(dp, head_dim, num_seqs, num_tokens, stream);
+  if (e == hipSuccess) e = stage(3, stream);
   if (e != hipSuccess) return fail_hip(e, "paged_attention decode launch");
 
   PrefillParams fp{};
@@ -283,6 +294,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   const int prefill_grid = (int)std::max<int64_t>(
       1, std::min<int64_t>((int64_t)dev.cus * dev.prefill_wg[di], prefill_wgs));
   e = launch_prefill(fp, head_dim, prefill_grid, stream);
+  if (e == hipSuccess) e = stage(4, stream);
   if (e != hipSuccess) return fail_hip(e, "paged_attention prefill launch");
   return PAGED_OK;
 }
@@ -353,6 +365,20 @@ int paged_attention_set_partition_tokens(int32_t tokens) {
   if (tokens != 0 && (tokens < 32 || tokens > 1024 || tokens % 32))
     return fail(PAGED_EINVAL, "partition tokens must be 0 or a multiple of 32 in [32, 1024]");
   g_part_tokens.store(tokens);
+  return PAGED_OK;
+}
+
+int paged_attention_set_stage_events(void* const* events, int32_t count) {
+  if (events == nullptr || count == 0) {
+    g_stage_on = false;
+    return PAGED_OK;
+  }
+  if (count != 5) return fail(PAGED_EINVAL, "stage events: count must be 0 or 5");
+  for (int i = 0; i < 5; ++i) {
+    if (!events[i]) return fail(PAGED_EINVAL, "stage events: null event %d", i);
+    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_stage_on = true;
   return PAGED_OK;
 }
 

@@ -298,15 +298,17 @@ decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
   }
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, int num_seqs,
-                         int num_tokens, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, hipStream_t stream) {
   if (head_dim == 128) {
     decode_kernel<128><<<grid, 256, 0, stream>>>(p);
   } else {
     decode_kernel<64><<<grid, 256, 0, stream>>>(p);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs, int num_tokens,
+                               hipStream_t stream) {
   const int hchunks = (p.hq + 3) / 4;
   const int rgrid = num_seqs * hchunks;
   if (rgrid == 0) return hipSuccess;

@@ -64,8 +64,9 @@ hipError_t launch_kv_write(const void* k, const void* v, const int32_t* slots, v
                            int64_t num_blocks, int64_t k_stride, int64_t v_stride,
                            hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, int num_seqs,
-                         int num_tokens, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs, int num_tokens,
+                               hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int grid, hipStream_t stream);
 const void* decode_kernel_ptr(int head_dim);
 const void* prefill_kernel_ptr(int head_dim);
