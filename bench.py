@@ -191,6 +191,21 @@ def prefill_cpu_baseline(wl):
             "sample": f"segment {s} ({n} tokens) of the prefill batch: {dt:.2f} s"}
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of ``nbytes``: it reads and writes
+    exactly ``nbytes`` each, so the counters it reads give the scale between
+    counter units and HBM bytes."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def make_workload(name):
     import torch
     import workloads
@@ -228,6 +243,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=160, help="decode requests the oracle runs")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times), the reference kernel "
+                         "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -240,6 +258,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     pkv.lib()
     if args.partition_tokens:
         pkv.paged_attention_set_partition_tokens(args.partition_tokens)

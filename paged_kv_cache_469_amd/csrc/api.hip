@@ -118,7 +118,7 @@ hipError_t device_info(DeviceInfo& out) {
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_kernel_ptr(hd), 256, 0);
       if (e != hipSuccess) return e;
       d.decode_wg[i] = std::max(1, nb);
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, prefill_kernel_ptr(hd), 256, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, prefill_kernel_ptr(hd), 512, 0);
       if (e != hipSuccess) return e;
       d.prefill_wg[i] = std::max(1, nb);
     }
@@ -220,8 +220,9 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   char* ws = static_cast<char*>(workspace);
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
   const int group = num_q_heads / num_kv_heads;
-  const int heads_per_item = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-  const int query_tile = 32 * (4 / heads_per_item);
+  // prefill: 8 waves of 32 queries; the heads of one item share the KV head
+  const int heads_per_item = group % 8 == 0 ? 8 : (group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1));
+  const int query_tile = 32 * (8 / heads_per_item);
   const float scale_log2 = scale * 1.4426950408889634f;
 
   PlanParams pp{};
@@ -289,11 +290,17 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   fp.group = group;
   fp.heads_per_item = heads_per_item;
   fp.head_chunks = group / heads_per_item;
-  fp.scale_log2 = scale_log2;
+  fp.query_tile = query_tile;
+  // KV head g is served by the queue of XCD g % 8 (workgroup i runs on XCD
+  // i % 8), so the workgroups reading one head's K/V share that XCD's L2
+  fp.num_queues = num_kv_heads % kMaxQueues == 0 ? kMaxQueues : 1;
+  // |scale| * log2(e), at least 1e-30 so masked logits (-inf) still map to 0
+  fp.c = std::max(std::fabs(scale_log2), 1e-30f);
+  fp.q_sign = scale_log2 < 0.f ? 0x80008000u : 0u;
   const int64_t prefill_wgs = l.prefill_cap * num_kv_heads * fp.head_chunks;
-  const int prefill_grid = (int)std::max<int64_t>(
-      1, std::min<int64_t>((int64_t)dev.cus * dev.prefill_wg[di], prefill_wgs));
-  e = launch_prefill(fp, head_dim, prefill_grid, stream);
+  int64_t prefill_grid = std::min<int64_t>((int64_t)dev.cus * dev.prefill_wg[di], prefill_wgs);
+  prefill_grid = std::max<int64_t>(fp.num_queues, prefill_grid / fp.num_queues * fp.num_queues);
+  e = launch_prefill(fp, head_dim, (int)prefill_grid, stream);
   if (e == hipSuccess) e = stage(4, stream);
   if (e != hipSuccess) return fail_hip(e, "paged_attention prefill launch");
   return PAGED_OK;

@@ -18,15 +18,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Workspace header: one 256-byte line at the start of the workspace.
+#define PKV_LDS __attribute__((address_space(3)))
+
+// Workspace header: one 256-byte line at the start of the workspace, rewritten
+// by the plan kernel on every call.
+constexpr int kMaxQueues = 8;   // prefill work queues, one per XCD when the KV heads split evenly
 struct WsHeader {
-  uint32_t status;          // PAGED_STATUS_* bits
-  int32_t n_decode;         // decode work items (segment, partition)
-  int32_t n_prefill;        // prefill work items (segment, query tile)
-  int32_t decode_next;      // dynamic scheduling counters
-  int32_t prefill_next;
-  int32_t pad[59];
+  uint32_t status;                  // PAGED_STATUS_* bits
+  int32_t n_decode;                 // decode work items (segment, partition)
+  int32_t n_prefill;                // prefill work items (segment, query tile)
+  int32_t decode_next;              // dynamic scheduling counter of the decode kernel
+  int32_t prefill_next[kMaxQueues]; // dynamic scheduling counters of the prefill kernel
+  int32_t pad0[4];
+  uint32_t zeros[16];               // 64 zero bytes: the source of K/V rows never loaded
+  int32_t pad1[32];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte line");
 

@@ -137,6 +137,7 @@ decode_kernel(DecodeParams p) {
   const int m = lane & 15;
   const int j = lane >> 4;
   const int n_items = p.hdr->n_decode * p.hkv;
+  if (n_items == 0) return;   // no decode segment in this step: no queue traffic
   const int64_t row_elems = (int64_t)p.hkv * D;
   const int64_t block_elems = 2 * kBlock * row_elems;
 

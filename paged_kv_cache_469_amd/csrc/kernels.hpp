@@ -49,14 +49,17 @@ struct PrefillParams {
   const int32_t* lens;
   uint16_t* out;
   WsHeader* hdr;
-  const int2* items;       // (segment, query tile)
+  const int2* items;       // (segment, query tile), most key tiles first
   int64_t q_stride;
   int64_t num_blocks;
   int32_t width;
   int32_t hq, hkv, group;
-  int32_t heads_per_item;  // HW: heads handled by one work item (1, 2 or 4)
+  int32_t heads_per_item;  // HW: query heads of one work item (1, 2 or 4), one per wave
   int32_t head_chunks;     // group / HW
-  float scale_log2;
+  int32_t query_tile;      // QT = 64 * 4 / HW queries per work item
+  int32_t num_queues;      // 8 (KV head g served by the XCD queue g % 8) or 1
+  float c;                 // |scale| * log2(e)
+  uint32_t q_sign;         // 0x80008000 when scale < 0 (queries negated), else 0
 };
 
 hipError_t launch_kv_write(const void* k, const void* v, const int32_t* slots, void* cache,

@@ -6,15 +6,20 @@
 // One workgroup of 1024 threads walks the segments on the device, so the
 // host never reads metadata and the whole call can be captured in a graph:
 //   n == 1 -> decode: ceil(L / P) items (segment, partition)
-//   n >  1 -> prefill: ceil(n / QT) items (segment, query tile), the tile
-//             with the most keys (the last) first
+//   n >  1 -> prefill: ceil(n / QT) items (segment, query tile)
 //   n == 0 -> nothing
-// Segments whose bounds are out of range are skipped and flagged.  It also
-// resets the status word and the dynamic-scheduling counters the attention
-// kernels use, so the workspace needs no clearing between calls.
+// Prefill items are ordered by their number of 64-key tiles, most first (a
+// counting sort over 1024 cost buckets), so the dynamic queues hand out the
+// longest work first and the short items fill the tail.  Segments whose
+// bounds are out of range are skipped and flagged.  The kernel also resets
+// the status word and the dynamic-scheduling counters and writes the zero
+// line of the header, so the workspace needs no clearing between calls.
 #include "kernels.hpp"
 
 namespace pkv {
+
+constexpr int kCostBuckets = 1024;
+constexpr int kPrefillTileKeys = 64;   // key tile of the prefill kernel
 
 // Exclusive prefix sum over the 1024 threads of the block; returns the
 // thread's offset and writes the block total to *total.
@@ -45,53 +50,99 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
   return res;
 }
 
+struct SegInfo {
+  int n, L;
+  bool ok;
+};
+
+__device__ __forceinline__ SegInfo seg_info(const PlanParams& p, int s) {
+  SegInfo r{0, 0, false};
+  if (s >= p.num_seqs) return r;
+  const int c0 = p.cu[s];
+  const int c1 = p.cu[s + 1];
+  r.L = p.lens[s];
+  r.n = c1 - c0;
+  r.ok = c0 >= 0 && c1 <= p.num_tokens && r.n >= 0 && r.L >= r.n && r.L <= p.max_len;
+  return r;
+}
+
+// Sort key of prefill item (query tile qt of a segment with n new tokens and
+// L total): bucket 0 holds the items with the most key tiles.
+__device__ __forceinline__ int cost_key(int n, int L, int qt, int qtile) {
+  const int kmax = L - n + min(n, (qt + 1) * qtile);
+  const int tiles = (kmax + kPrefillTileKeys - 1) / kPrefillTileKeys;
+  return kCostBuckets - 1 - min(tiles, kCostBuckets - 1);
+}
+
 __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   __shared__ int scratch[17];
+  __shared__ int hist[kCostBuckets];
+  hist[threadIdx.x] = 0;   // blockDim.x == kCostBuckets
+  if (threadIdx.x < 16) p.hdr->zeros[threadIdx.x] = 0u;
+  __syncthreads();
+
+  // pass 1: decode items in segment order; prefill item count and cost histogram
   int dec_base = 0;
-  int pre_base = 0;
+  int pre_total = 0;
   uint32_t status = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
-    int nd = 0, np = 0, L = 0, n = 0;
-    if (s < p.num_seqs) {
-      const int c0 = p.cu[s];
-      const int c1 = p.cu[s + 1];
-      L = p.lens[s];
-      n = c1 - c0;
-      const bool ok = c0 >= 0 && c1 <= p.num_tokens && n >= 0 && L >= n && L <= p.max_len;
-      if (!ok) {
-        status |= 1u;
-      } else if (n == 1) {
-        nd = (L + p.part_tokens - 1) / p.part_tokens;
-      } else if (n > 1) {
-        np = (n + p.query_tile - 1) / p.query_tile;
-      }
+    const SegInfo si = seg_info(p, s);
+    int nd = 0, np = 0;
+    if (s < p.num_seqs && !si.ok) {
+      status |= 1u;
+    } else if (si.ok && si.n == 1) {
+      nd = (si.L + p.part_tokens - 1) / p.part_tokens;
+    } else if (si.ok && si.n > 1) {
+      np = (si.n + p.query_tile - 1) / p.query_tile;
+      for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
     }
     int tot_d, tot_p;
     const int od = dec_base + block_exclusive_scan(nd, scratch, &tot_d);
-    const int op = pre_base + block_exclusive_scan(np, scratch, &tot_p);
+    block_exclusive_scan(np, scratch, &tot_p);
     // overlapping segments (only possible when some segment is malformed)
     // could overflow the lists: items past the capacity are dropped and flagged
     for (int i = 0; i < nd; ++i)
       if (od + i < p.decode_cap) p.decode_items[od + i] = make_int2(s, i);
-    for (int i = 0; i < np; ++i)
-      if (op + i < p.prefill_cap) p.prefill_items[op + i] = make_int2(s, np - 1 - i);
-    if (od + nd > p.decode_cap || op + np > p.prefill_cap) status |= 1u;
+    if (od + nd > p.decode_cap) status |= 1u;
     dec_base += tot_d;
-    pre_base += tot_p;
+    pre_total += tot_p;
   }
+  if (pre_total > p.prefill_cap) status |= 1u;
+  __syncthreads();
+
+  // pass 2: bucket offsets (exclusive scan of the histogram)
+  int unused;
+  hist[threadIdx.x] = block_exclusive_scan(hist[threadIdx.x], scratch, &unused);
+  __syncthreads();
+
+  // pass 3: scatter prefill items to their bucket's next place
+  if (pre_total > 0) {
+    for (int base = 0; base < p.num_seqs; base += 1024) {
+      const int s = base + (int)threadIdx.x;
+      const SegInfo si = seg_info(p, s);
+      if (si.ok && si.n > 1) {
+        const int np = (si.n + p.query_tile - 1) / p.query_tile;
+        for (int qt = 0; qt < np; ++qt) {
+          const int at = atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
+          if (at < p.prefill_cap) p.prefill_items[at] = make_int2(s, qt);
+        }
+      }
+    }
+  }
+
   const int any_bad = __syncthreads_or((int)status);
   if (threadIdx.x == 0) {
     p.hdr->status = any_bad ? 1u : 0u;
     p.hdr->n_decode = min(dec_base, p.decode_cap);
-    p.hdr->n_prefill = min(pre_base, p.prefill_cap);
+    p.hdr->n_prefill = min(pre_total, p.prefill_cap);
     p.hdr->decode_next = 0;
-    p.hdr->prefill_next = 0;
   }
+  if (threadIdx.x < kMaxQueues) p.hdr->prefill_next[threadIdx.x] = 0;
 }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
-  plan_kernel<<<1, 1024, 0, stream>>>(p);
+  plan_kernel<<<1, kCostBuckets, 0, stream>>>(p);
   return hipGetLastError();
 }
 

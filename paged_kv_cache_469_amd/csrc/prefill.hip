@@ -6,269 +6,424 @@
 // long prompt) attends causally: query i sees keys 0 .. h + i of its own
 // sequence, read through its block table.  Prefill is a dense contraction
 // ("从0开始的vLLM学习": prefill is compute bound), so both products run on
-// the bf16 matrix cores.
+// the bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Work item: (segment, query tile, KV head, head chunk), run by a workgroup
-// of 4 waves.  Each wave owns one query head and 32 queries; the 4 waves of a
-// workgroup share the KV head, so each 64-key K/V tile is gathered from its
-// four 16-token blocks once into LDS and used by all of them.  Per wave, per
-// 32 keys:
-//   S^T[key, q] = K[key, :] . Q[q, :]        32x32x16 bf16 MFMA over D/16 slabs
-//   causal mask (only on tiles that cross the diagonal), online softmax in
-//   fp32 with exp2 (scale*log2(e) folded in)
-//   O^T[d, q] += V^T[d, key] . P^T[key, q]   32x32x16 bf16 MFMA, D/32 d tiles
-// The C layout of S^T (lane = query, 16 keys per lane) is the B operand layout
-// of the second product, so P stays in registers.  LDS rows are XOR-swizzled
-// in 16-byte chunks by row so the K operand reads (32 rows, one chunk each)
-// and the V reads are free of bank conflicts; V is read with a permuted d
-// order (tile t, row m <-> d = (D/32)*m + t) and transposed with v_perm.
-// Keys at or past L are written to LDS as zeros, never loaded.
+// Work item: (segment, query tile of QT queries, KV head, head chunk), run by
+// one workgroup of 8 waves, two per SIMD.  Each wave owns one query head and
+// 32 queries; the waves share the KV head, so each 64-key K/V tile is copied
+// from its four 16-token blocks once, straight from global memory into LDS
+// (global_load_lds_dwordx4), and read by all eight.
+//
+// Per wave and tile:
+//   S^T[key, q] = K[key, :] . Q[q, :]         Q held in registers (B operand)
+//   P = exp2(S * c - m * c) in fp32 -> bf16   c = |scale| * log2(e)
+//   O^T[d, q] += V^T[d, key] . P^T[key, q]    V^T fragments come from the
+//                                             transposing LDS read
+//                                             (ds_read_b64_tr_b16)
+// The C layout of S^T (lane = query) is the B operand layout of the second
+// product, so P never leaves registers.  The running maximum m is lazy: it
+// moves only when a tile's maximum exceeds it by more than 8 (log2 units),
+// so rescaling O is rare and P stays below 2^8; the normaliser l sums the
+// bf16-rounded P that the numerator uses.
+//
+// Ping-pong: waves 0-3 (group A) and 4-7 (group B) sit on the four SIMDs in
+// pairs and alternate phases, separated by workgroup barriers.  While group
+// A issues the matrix products of tile t (QK^T of t, PV of t-1), group B runs
+// the softmax of tile t-1 on the vector ALUs of the same SIMDs, and then the
+// other way round; so the matrix cores and the vector ALUs work at the same
+// time.  K of tile t+1 and V of tile t are copied while tile t is processed
+// (two slots each).  K/V rows at or past L, and rows of blocks outside the
+// pool, come from a zero line, so poison in unused pool memory never reaches
+// the products.
 #include "kernels.hpp"
 
 namespace pkv {
+namespace {
 
-constexpr int kTileKeys = 64;
+constexpr int kKeys = 64;           // keys per tile
+constexpr int kWaves = 8;
+constexpr float kLazyMax = 8.f;     // how far (log2 units) m may trail the true maximum
 
 template <int D>
-struct PrefillTile {
-  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int CHUNKS = kTileKeys * CPR;       // per K (or V) tile
-  static constexpr int PER_THREAD = CHUNKS / 256;      // 4 for D = 128
-  static constexpr int ELEMS = kTileKeys * D;          // bf16 per K (or V) tile
+struct Geo {
+  static constexpr int ROWB = 2 * D;           // bytes of one key row of a head
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int TILEB = kKeys * ROWB;   // bytes of one K or V tile
+  static constexpr int NSL = D / 16;           // d slabs of QK^T
+  static constexpr int NDT = D / 32;           // d tiles of PV
+  static constexpr int RPI = 1024 / ROWB;      // rows one wave-wide 16-byte LDS copy fills
+  static constexpr int RPW = kKeys / (kWaves / 2);   // rows of a tile each copying wave fills
+  static constexpr int LPW = RPW / RPI;        // copies per wave per tile and half
+  static_assert(LPW >= 1 && RPW % RPI == 0, "tile rows must split evenly over the waves");
 };
 
+// Chunk c (16 bytes) of K row r sits at chunk c ^ (r % CPR): the rows one
+// quarter-wave reads with 16-byte operand loads hit different banks.
 template <int D>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * D + ((chunk ^ (row & (PrefillTile<D>::CPR - 1))) << 3);
+__device__ __forceinline__ int k_chunk(int r, int c) {
+  return c ^ (r & (Geo<D>::CPR - 1));
 }
 
+// Chunk c of V row r sits at chunk c ^ s(r % 4), s = 0, 4, 10, 14 (mod CPR):
+// the transposing reads take 4 consecutive rows x 32 or 64 bytes at once,
+// and these land on disjoint banks.
 template <int D>
-__device__ __forceinline__ void gather_tile(u32x4 (&kr)[PrefillTile<D>::PER_THREAD],
-                                            u32x4 (&vr)[PrefillTile<D>::PER_THREAD],
-                                            const PrefillParams& p, const int32_t* bt_row,
-                                            int k0, int L, int g, int64_t row_elems,
-                                            int64_t block_elems, uint32_t& bad) {
-  constexpr int CPR = PrefillTile<D>::CPR;
-#pragma unroll
-  for (int i = 0; i < PrefillTile<D>::PER_THREAD; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    const int row = c / CPR;
-    const int ch = c % CPR;
-    const int key = k0 + row;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    kr[i] = z;
-    vr[i] = z;
-    if (key < L) {
-      const int bid = bt_row[key / kBlock];
-      if (bid >= 0 && (int64_t)bid < p.num_blocks) {
-        const uint16_t* src = p.cache + (int64_t)bid * block_elems +
-                              (int64_t)(key % kBlock) * row_elems + (int64_t)g * D + ch * 8;
-        kr[i] = *reinterpret_cast<const u32x4*>(src);
-        vr[i] = *reinterpret_cast<const u32x4*>(src + kBlock * row_elems);
-      } else {
-        bad = 1;
-      }
-    }
-  }
+__device__ __forceinline__ int v_chunk(int r, int c) {
+  const int s = (r & 3) * 4 + ((r >> 1) & 1) * 2;
+  return c ^ (s & (Geo<D>::CPR - 1));
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(uint16_t* lk, uint16_t* lv,
-                                           const u32x4 (&kr)[PrefillTile<D>::PER_THREAD],
-                                           const u32x4 (&vr)[PrefillTile<D>::PER_THREAD]) {
-  constexpr int CPR = PrefillTile<D>::CPR;
-#pragma unroll
-  for (int i = 0; i < PrefillTile<D>::PER_THREAD; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    const int at = swz<D>(c / CPR, c % CPR);
-    *reinterpret_cast<u32x4*>(lk + at) = kr[i];
-    *reinterpret_cast<u32x4*>(lv + at) = vr[i];
-  }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
-template <int D>
-__global__ void __launch_bounds__(256)
-prefill_kernel(PrefillParams p) {
-  constexpr int NSL = D / 16;    // k slabs of the QK product
-  constexpr int NDT = D / 32;    // d tiles of the PV product
-  constexpr int CPR = PrefillTile<D>::CPR;
-  constexpr int PT = PrefillTile<D>::PER_THREAD;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][PrefillTile<D>::ELEMS];
-  __shared__ int s_item;
+// Combine a value with the other half of the wave (lane l and l ^ 32).
+// v_permlane32_swap on two copies of x leaves x's low half in both halves of
+// one copy and its high half in both halves of the other.  Written as inline
+// asm: through the builtin, the compiler keeps only one of the two results
+// when both operands hold the same value.  The s_nop covers the wait the
+// instruction needs after a VALU write of its operands.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  float lo, hi;
+  halves(x, lo, hi);
+  return lo + hi;
+}
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int col = lane & 31;     // query within the wave's 32
-  const int j = lane >> 5;       // k group of the MFMA operands
-  const int per_tile = p.hkv * p.head_chunks;
-  const int n_items = p.hdr->n_prefill * per_tile;
+// Workgroup barrier with no memory wait of its own; the empty asm statements
+// keep the compiler from moving memory accesses across it and the scheduling
+// barriers keep every other instruction on its side.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Wait until this wave's global -> LDS copies have landed (vmcnt(0)).
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Issue the global -> LDS copies of this wave's rows of tile t: K into dst
+// (VHALF false) or V (VHALF true).  LDS address 0 is a valid slot, so a slot
+// pointer never doubles as a flag.
+template <int D, bool VHALF>
+__device__ __forceinline__ void load_rows(const PrefillParams& p, const int32_t* bt_row, int t,
+                                          int L, int g, int wave, int lane, PKV_LDS char* dst_slot,
+                                          uint32_t& bad) {
+  using G = Geo<D>;
+  const int r0 = G::RPW * wave;                  // first tile row of this wave
+  const int blk = 4 * t + r0 / kBlock;
+  const int key0 = kKeys * t + r0;               // first key of this wave's rows
+  const bool exists = key0 < L;
+  const int bid = exists ? bt_row[blk] : -1;
+  const bool ok = exists && bid >= 0 && (int64_t)bid < p.num_blocks;
+  if (exists && !ok) bad = 1;
   const int64_t row_elems = (int64_t)p.hkv * D;
-  const int64_t block_elems = 2 * kBlock * row_elems;
-  const int qblocks = 4 / p.heads_per_item;   // 32-query blocks per item
-
-  for (;;) {
-    if (tid == 0) s_item = atomicAdd(&p.hdr->prefill_next, 1);
-    __syncthreads();
-    const int it = s_item;
-    __syncthreads();
-    if (it >= n_items) break;
-    const int2 item = p.items[it / per_tile];
-    const int sub = it % per_tile;
-    const int g = sub / p.head_chunks;
-    const int hc = sub % p.head_chunks;
-    const int s = item.x;
-    const int qt = item.y;
-    const int L = p.lens[s];
-    const int tok0 = p.cu[s];
-    const int n = p.cu[s + 1] - tok0;
-    const int h = L - n;
-    const int head = g * p.group + hc * p.heads_per_item + (wave % p.heads_per_item);
-    const int qb0 = (qt * qblocks + wave / p.heads_per_item) * 32;   // first query of the wave
-    const int q_item_end = min(n, (qt + 1) * qblocks * 32);
-    const int kmax = h + q_item_end;                                  // keys the item needs
-    const int qi = qb0 + col;
-    const int lim = h + min(qi, n - 1);                               // last key this lane sees
-    const int32_t* bt_row = p.bt + (int64_t)s * p.width;
-
-    u32x4 qf[NSL];
-    {
-      const uint16_t* qrow = p.q + (int64_t)(tok0 + qi) * p.q_stride + (int64_t)head * D + 8 * j;
+  const uint16_t* base = p.cache + (ok ? (int64_t)bid * 2 * kBlock * row_elems : 0) +
+                         (int64_t)(r0 % kBlock) * row_elems + (int64_t)g * D;
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(p.hdr->zeros);
 #pragma unroll
-      for (int sl = 0; sl < NSL; ++sl) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qf[sl] = qi < n ? *reinterpret_cast<const u32x4*>(qrow + 16 * sl) : z;
+  for (int i = 0; i < G::LPW; ++i) {
+    const int rr = G::RPI * i + lane / G::CPR;   // row among this wave's rows
+    const int r = r0 + rr;                       // row within the tile
+    const int pc = lane % G::CPR;                // chunk this lane fills
+    const bool live = ok && key0 + rr < L;
+    const int dst = (r0 + G::RPI * i) * G::ROWB;
+    const uint16_t* src = VHALF ? base + (kBlock + rr) * row_elems + 8 * v_chunk<D>(r, pc)
+                                : base + rr * row_elems + 8 * k_chunk<D>(r, pc);
+    __builtin_amdgcn_global_load_lds(live ? src : zero, dst_slot + dst, 16, 0, 0);
+  }
+}
+
+// Order of a matrix phase: a few LDS reads ahead, then one MFMA per read
+// (two reads per MFMA for the transposed V operand), so only a handful of
+// operand fragments are live at a time.
+template <int MFMAS, int READS, int LEAD>
+__device__ __forceinline__ void pipe_order() {
+#pragma unroll
+  for (int i = 0; i < LEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+  for (int i = 0; i < MFMAS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + LEAD < MFMAS) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  }
+}
+
+// S^T of this wave's 32 queries over the two 32-key halves of the K tile `kt_lds`.
+template <int D>
+__device__ __forceinline__ void qk(f32x16 (&s)[2], const u32x4 (&q)[Geo<D>::NSL],
+                                   const uint32_t (&ak)[Geo<D>::NSL], const PKV_LDS char* kt_lds) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int sl = 0; sl < G::NSL; ++sl) {
+      const u32x4 k =
+          *reinterpret_cast<const PKV_LDS u32x4*>(kt_lds + ak[sl] + kt * 32 * G::ROWB);
+      s[kt] = mfma32(k, q[sl], sl == 0 ? f32x16{} : s[kt]);
+    }
+  }
+  pipe_order<2 * G::NSL, 1, 3>();
+}
+
+// O^T += V^T P^T over the V tile `vt_lds`.
+template <int D>
+__device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2][2],
+                                   const uint32_t (&av)[Geo<D>::NDT], const PKV_LDS char* vt_lds) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt) {
+        const PKV_LDS char* at = vt_lds + av[dt] + (32 * kt + 16 * u) * G::ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4*)at);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PKV_LDS i16x4*)(at + 8 * G::ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        o[dt] = mfma32(u32x4{l2[0], l2[1], h2[0], h2[1]}, pr[kt][u], o[dt]);
       }
     }
-    f32x16 o[NDT];
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) o[t] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    uint32_t bad = 0;
+  }
+  pipe_order<4 * G::NDT, 2, 3>();
+}
 
-    const int ntiles = (kmax + kTileKeys - 1) / kTileKeys;
-    u32x4 kr[PT], vr[PT];
-    gather_tile<D>(kr, vr, p, bt_row, 0, L, g, row_elems, block_elems, bad);
-    store_tile<D>(lds[0][0], lds[0][1], kr, vr);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-      const int k0 = t * kTileKeys;
-      if (t + 1 < ntiles)
-        gather_tile<D>(kr, vr, p, bt_row, k0 + kTileKeys, L, g, row_elems, block_elems, bad);
-      const uint16_t* lk = lds[t & 1][0];
-      const uint16_t* lv = lds[t & 1][1];
-
-      // S^T for the two 32-key halves of the tile
-      f32x16 sc[2];
+// Online softmax of one tile's scores (keys k0 ..): updates the lazy maximum
+// and the row sum, rescales O when the maximum moved, and packs P as the
+// bf16 B operands of PV.  With MASK, keys past lim (per lane) are dropped.
+template <int D, bool MASK>
+__device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], f32x16 (&o)[Geo<D>::NDT],
+                                        float& m, float& l, float c, int k0, int lim, int lane) {
+  const int h = lane >> 5;
+  constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 (1, 1)
+  if constexpr (MASK) {
+    // key of register r of half kt = k0 + 4h + (32kt + 8(r/4) + r%4); the
+    // distance t = lim - key is compared with 0 in float arithmetic: a
+    // dropped key gets t * 1e38 <= -1e38 added (-inf for t <= -4), a kept one
+    // gets 0.  No lane masks or selects, and the scores are finite, so no NaN.
+    const float fb = (float)(lim - k0 - 4 * h);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sc[kt] = f32x16{};
-        const int row = kt * 32 + col;
-#pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(lk + swz<D>(row, 2 * sl + j));
-          sc[kt] = mfma32(a, qf[sl], sc[kt]);
-        }
-      }
-      // scores, causal mask where the tile crosses this wave's diagonal
-      const bool need_mask = k0 + kTileKeys - 1 > h + qb0;
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sc[kt][r] * p.scale_log2;
-          if (need_mask) {
-            const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * j + (r & 3);
-            x = key <= lim ? x : -INFINITY;
-          }
-          sc[kt][r] = x;
-          cmax = fmaxf(cmax, x);
-        }
-      }
-      cmax = wave_max_xor(cmax, 32);
-      const float m_new = fmaxf(m_run, cmax);
-      const float alpha = exp2f(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = exp2f(sc[kt][r] - m_new);
-          sc[kt][r] = e;
-          psum += e;
-        }
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-
-      // O^T += V^T P^T over four 16-key slabs
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 pb = {pack_bf16(sc[kt][8 * u + 0], sc[kt][8 * u + 1]),
-                            pack_bf16(sc[kt][8 * u + 2], sc[kt][8 * u + 3]),
-                            pack_bf16(sc[kt][8 * u + 4], sc[kt][8 * u + 5]),
-                            pack_bf16(sc[kt][8 * u + 6], sc[kt][8 * u + 7])};
-          // lane's V pieces: 8 keys x (D/32) consecutive d starting at (D/32)*col
-          uint32_t vv[8][NDT / 2 > 0 ? NDT / 2 : 1];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int row = kt * 32 + 16 * u + 8 * (e >> 2) + 4 * j + (e & 3);
-            const int d0 = NDT * col;
-            const uint16_t* src = lv + swz<D>(row, d0 >> 3) + (d0 & 7);
-            if constexpr (NDT == 4) {
-              const u32x2 x = *reinterpret_cast<const u32x2*>(src);
-              vv[e][0] = x[0];
-              vv[e][1] = x[1];
-            } else {
-              vv[e][0] = *reinterpret_cast<const uint32_t*>(src);
-            }
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int w = dt >> 1;
-            const bool hi = dt & 1;
-            const u32x4 a = {pick_halves(vv[0][w], vv[1][w], hi), pick_halves(vv[2][w], vv[3][w], hi),
-                             pick_halves(vv[4][w], vv[5][w], hi), pick_halves(vv[6][w], vv[7][w], hi)};
-            o[dt] = mfma32(a, pb, o[dt]);
-          }
-        }
-      }
-      if (t + 1 < ntiles) store_tile<D>(lds[(t + 1) & 1][0], lds[(t + 1) & 1][1], kr, vr);
-      __syncthreads();
-    }
-    if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
-
-    l_run += __shfl_xor(l_run, 32);
-    if (qi < n) {
-      const float inv = 1.f / l_run;
-      uint16_t* orow = p.out + ((int64_t)(tok0 + qi) * p.hq + head) * D;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int drow = 8 * (r >> 2) + 4 * j + (r & 3);
-        uint16_t* dst = orow + NDT * drow;
-        if constexpr (NDT == 4) {
-          *reinterpret_cast<u32x2*>(dst) =
-              u32x2{pack_bf16(o[0][r] * inv, o[1][r] * inv), pack_bf16(o[2][r] * inv, o[3][r] * inv)};
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = pack_bf16(o[0][r] * inv, o[1][r] * inv);
-        }
+        const float t = fb - (float)(32 * kt + 8 * (r >> 2) + (r & 3));
+        s[kt][r] = fmaf(fminf(t, 0.f), 1e38f, s[kt][r]);
       }
+  }
+  float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  mx = halves_max(mx);
+  const bool first = m == -INFINITY;
+  const bool upd = first || (mx - m) * c > kLazyMax;
+  if (__builtin_amdgcn_ballot_w64(upd)) {
+    const float mn = upd ? mx : m;
+    const float alpha = first ? 0.f : (upd ? fast_exp2((m - mn) * c) : 1.f);
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < Geo<D>::NDT; ++dt) o[dt] *= alpha;
+  }
+  const float mc = m * c;
+  float ls = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 8 * u + 2 * i;
+        w[i] = pack_bf16(fast_exp2(fmaf(s[kt][r], c, -mc)), fast_exp2(fmaf(s[kt][r + 1], c, -mc)));
+        ls = dot2_bf16(w[i], kOnes, ls);
+      }
+      pr[kt][u] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+  l += ls;
+}
+
+// Everything one wave needs for one work item.
+template <int D>
+struct Item {
+  const int32_t* bt_row;
+  int L, n, h, g, head, qw, ntiles, kfull, kend, lim, qi;
+  bool active;
+};
+
+// LDS slots: K and V of two tiles, as four separate objects so the compiler
+// can tell that a copy into one slot never touches the slot being read.
+template <int D>
+struct Slots {
+  PKV_LDS char* k[2];
+  PKV_LDS char* v[2];
+};
+
+// One tile step t (PAR = t % 2) of one wave: QK(t) and PV(t-1) on the
+// matrix cores, a barrier, the softmax of tile t, a barrier.  Group B runs
+// the same sequence one phase later (it passes one extra barrier first), so
+// each SIMD pairs one wave's matrix phase with the other's softmax.  Group A
+// copies K(t+1) and V(t) at the start of its step and waits for them at the
+// end: the first readers of K(t+1) and V(t) come after that barrier, and the
+// slots they overwrite were last read by group B before the step began.
+template <int D, int PAR>
+__device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>& it, const Slots<D>& sl,
+                                          int t, bool group_b, int wave, int lane,
+                                          const u32x4 (&q)[Geo<D>::NSL], f32x16 (&o)[Geo<D>::NDT],
+                                          f32x16 (&sc)[2], u32x4 (&pr)[2][2], float& m, float& l,
+                                          const uint32_t (&ak)[Geo<D>::NSL],
+                                          const uint32_t (&av)[Geo<D>::NDT], uint32_t& bad) {
+  if (!group_b) {
+    if (t + 1 < it.ntiles)
+      load_rows<D, false>(p, it.bt_row, t + 1, it.L, it.g, wave, lane, sl.k[1 - PAR], bad);
+    if (t < it.ntiles) load_rows<D, true>(p, it.bt_row, t, it.L, it.g, wave, lane, sl.v[PAR], bad);
+  }
+  // tile t for QK / softmax, tile t - 1 for PV; tiles no query of the wave sees are skipped
+  const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
+  const bool do_prev = it.active && t >= 1 && kKeys * (t - 1) < it.kend;
+  if (do_t) qk<D>(sc, q, ak, sl.k[PAR]);
+  if (do_prev) pv<D>(o, pr, av, sl.v[1 - PAR]);
+  wg_barrier();
+  if (do_t) {
+    if (kKeys * t + kKeys > it.kfull) softmax<D, true>(sc, pr, o, m, l, p.c, kKeys * t, it.lim, lane);
+    else softmax<D, false>(sc, pr, o, m, l, p.c, kKeys * t, it.lim, lane);
+  }
+  if (!group_b) wait_copies();
+  wg_barrier();
+}
+
+template <int D>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+prefill_kernel(PrefillParams p) {
+  using G = Geo<D>;
+  __shared__ __attribute__((aligned(1024))) char k0_lds[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k1_lds[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v0_lds[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v1_lds[G::TILEB];
+  __shared__ int s_item;
+  const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds},
+                       {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds}};
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool group_b = wave >= kWaves / 2;
+  const int hw = p.heads_per_item;
+  const int per_entry = (p.hkv / p.num_queues) * p.head_chunks;
+  const int queue = blockIdx.x % p.num_queues;
+  const int n_items = p.hdr->n_prefill * per_entry;
+  if (n_items == 0) return;   // no prefill segment in this step
+
+  // per-lane LDS addresses within a slot
+  uint32_t ak[G::NSL], av[G::NDT];
+  {
+    const int hh = lane >> 5;
+    const int r = lane & 31;
+#pragma unroll
+    for (int i = 0; i < G::NSL; ++i) ak[i] = r * G::ROWB + 16 * k_chunk<D>(r, 2 * i + hh);
+    const int rr = 4 * hh + ((lane & 15) >> 2);   // row within a 16-key slab
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) {
+      const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      av[dt] = rr * G::ROWB + 16 * v_chunk<D>(rr, d >> 3) + 2 * (d & 7);
+    }
+  }
+
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(&p.hdr->prefill_next[queue], 1);
+    __syncthreads();
+    const int itx = s_item;
+    __syncthreads();
+    if (itx >= n_items) break;
+    const int2 entry = p.items[itx / per_entry];
+    const int sub = itx % per_entry;
+    const int hc = sub % p.head_chunks;
+    const int s = entry.x;
+    const int qt = entry.y;
+    Item<D> it;
+    it.g = queue + p.num_queues * (sub / p.head_chunks);
+    it.L = p.lens[s];
+    const int tok0 = p.cu[s];
+    it.n = p.cu[s + 1] - tok0;
+    it.h = it.L - it.n;
+    it.head = it.g * p.group + hc * hw + wave % hw;
+    it.qw = qt * p.query_tile + (wave / hw) * 32;                 // first query of this wave
+    const int kmax = it.h + min(it.n, (qt + 1) * p.query_tile);   // keys the item needs
+    it.ntiles = (kmax + kKeys - 1) / kKeys;
+    it.active = it.qw < it.n;                                     // wave has real queries
+    it.kfull = it.h + it.qw + 1;                                  // keys all its queries see
+    it.kend = it.h + min(it.n - 1, it.qw + 31) + 1;               // keys some query sees
+    it.bt_row = p.bt + (int64_t)s * p.width;
+    it.qi = it.qw + (lane & 31);
+    it.lim = it.h + it.qi;
+    uint32_t bad = 0;
+
+    u32x4 q[G::NSL];
+    {
+      const uint16_t* qrow =
+          p.q + (int64_t)(tok0 + it.qi) * p.q_stride + (int64_t)it.head * D + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < G::NSL; ++i) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (it.qi < it.n) v = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
+        q[i] = v ^ p.q_sign;
+      }
+    }
+    f32x16 o[G::NDT];
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+    f32x16 sc[2];
+    u32x4 pr[2][2];
+
+    if (!group_b) load_rows<D, false>(p, it.bt_row, 0, it.L, it.g, wave, lane, sl.k[0], bad);
+    __syncthreads();   // K(0) in LDS; every wave done with the previous item's slots
+    if (group_b) wg_barrier();
+    for (int t = 0; t <= it.ntiles; t += 2) {
+      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, m, l, ak, av, bad);
+      if (t + 1 <= it.ntiles)
+        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, m, l, ak, av, bad);
+    }
+    if (!group_b) wg_barrier();
+    if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
+
+    // normalise and store: lane holds query qi, d = 32dt + 8i + 4(lane/32) + 0..3
+    const float lt = halves_sum(l);
+    if (it.qi < it.n) {
+      const float inv = 1.f / lt;
+      uint16_t* orow = p.out + ((int64_t)(tok0 + it.qi) * p.hq + it.head) * D + 4 * (lane >> 5);
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * i) =
+              u32x2{pack_bf16(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv),
+                    pack_bf16(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv)};
     }
   }
 }
+
+}  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, int grid, hipStream_t stream) {
   if (head_dim == 128) {
-    prefill_kernel<128><<<grid, 256, 0, stream>>>(p);
+    prefill_kernel<128><<<grid, 512, 0, stream>>>(p);
   } else {
-    prefill_kernel<64><<<grid, 256, 0, stream>>>(p);
+    prefill_kernel<64><<<grid, 512, 0, stream>>>(p);
   }
   return hipGetLastError();
 }
