@@ -25,13 +25,23 @@ FLAGS = [
 ]
 
 
+# Extra flags per source.  The prefill kernel keeps two waves per SIMD at the
+# 256-register limit; the iterative-ILP machine scheduler issues its LDS
+# operand reads several MFMAs ahead instead of one at a time.  Its scores are
+# never NaN (unused rows come from a zero line), so fmaxf needs no NaN
+# quieting of its operands (-fno-honor-nans; infinities are still honoured).
+PER_FILE = {
+    "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp", "-fno-honor-nans"],
+}
+
+
 def _hipcc():
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

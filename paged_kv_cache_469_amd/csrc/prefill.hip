@@ -11,8 +11,10 @@
 // Work item: (segment, query tile of QT queries, KV head, head chunk), run by
 // one workgroup of 8 waves, two per SIMD.  Each wave owns one query head and
 // 32 queries; the waves share the KV head, so each 64-key K/V tile is copied
-// from its four 16-token blocks once, straight from global memory into LDS
-// (global_load_lds_dwordx4), and read by all eight.
+// from its four 16-token blocks once into LDS and read by all eight.  The
+// copy is staged through registers: wave w of group A loads K of block w of
+// the tile, wave w of group B loads V of it, and each writes its block into
+// swizzled LDS rows a step later.
 //
 // Per wave and tile:
 //   S^T[key, q] = K[key, :] . Q[q, :]         Q held in registers (B operand)
@@ -31,8 +33,8 @@
 // A issues the matrix products of tile t (QK^T of t, PV of t-1), group B runs
 // the softmax of tile t-1 on the vector ALUs of the same SIMDs, and then the
 // other way round; so the matrix cores and the vector ALUs work at the same
-// time.  K of tile t+1 and V of tile t are copied while tile t is processed
-// (two slots each).  K/V rows at or past L, and rows of blocks outside the
+// time.  Loads run two tiles ahead and LDS writes one tile ahead, so each
+// of K and V has two LDS slots.  K/V rows at or past L, and rows of blocks outside the
 // pool, come from a zero line, so poison in unused pool memory never reaches
 // the products.
 #include "kernels.hpp"
@@ -51,10 +53,7 @@ struct Geo {
   static constexpr int TILEB = kKeys * ROWB;   // bytes of one K or V tile
   static constexpr int NSL = D / 16;           // d slabs of QK^T
   static constexpr int NDT = D / 32;           // d tiles of PV
-  static constexpr int RPI = 1024 / ROWB;      // rows one wave-wide 16-byte LDS copy fills
-  static constexpr int RPW = kKeys / (kWaves / 2);   // rows of a tile each copying wave fills
-  static constexpr int LPW = RPW / RPI;        // copies per wave per tile and half
-  static_assert(LPW >= 1 && RPW % RPI == 0, "tile rows must split evenly over the waves");
+  static_assert(kKeys == kBlock * (kWaves / 2), "each wave of a group copies one block per tile");
 };
 
 // Chunk c (16 bytes) of K row r sits at chunk c ^ (r % CPR): the rows one
@@ -114,39 +113,85 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Wait until this wave's global -> LDS copies have landed (vmcnt(0)).
-__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// A window of 64 consecutive block-table entries of the item, one per lane,
+// read with a vector load (so the tile loop issues no scalar memory loads,
+// which would force every LDS wait in it to drain the whole lgkm counter).
+struct BtWindow {
+  int base;    // first block of the window
+  int val;     // this lane's entry: block base + lane, or -1 past the table end
+  __device__ __forceinline__ void load(const int32_t* bt_row, int first, int nblk, int lane) {
+    base = first;
+    val = first + lane < nblk ? bt_row[first + lane] : -1;
+  }
+  // entry of block blk; blk - base must be in [0, 64)
+  __device__ __forceinline__ int get(int blk) const {
+    return __builtin_amdgcn_readlane(val, blk - base);
+  }
+};
 
-// Issue the global -> LDS copies of this wave's rows of tile t: K into dst
-// (VHALF false) or V (VHALF true).  LDS address 0 is a valid slot, so a slot
-// pointer never doubles as a flag.
-template <int D, bool VHALF>
-__device__ __forceinline__ void load_rows(const PrefillParams& p, const int32_t* bt_row, int t,
-                                          int L, int g, int wave, int lane, PKV_LDS char* dst_slot,
-                                          uint32_t& bad) {
+// Register-staged copy of one 16-key block: group A's wave w stages K of
+// block 4t + w, group B's wave 4 + w stages V of that block, NCH 16-byte
+// chunks per lane, and writes them into the swizzled LDS rows 16w .. 16w+15.
+// (Copying straight from global memory into LDS would leave a copy in
+// flight while the same wave reads its operands from LDS, and the compiler
+// then has to drain every LDS read before each use.)
+template <int D>
+struct Stage {
+  static constexpr int NCH = kBlock * Geo<D>::CPR / 64;
+  u32x4 r[NCH];
+};
+
+// Per-lane byte offsets of the staged chunks: g into the block (from the
+// start of its K half), s into the LDS slot.
+struct StageOff {
+  uint32_t g[4], s[4];
+};
+
+template <int D>
+__device__ __forceinline__ StageOff stage_offsets(bool vhalf, int wq, int lane, uint32_t row_bytes) {
   using G = Geo<D>;
-  const int r0 = G::RPW * wave;                  // first tile row of this wave
-  const int blk = 4 * t + r0 / kBlock;
-  const int key0 = kKeys * t + r0;               // first key of this wave's rows
+  static_assert(Stage<D>::NCH <= 4, "chunks per lane");
+  StageOff o;
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int j = lane + 64 * i;
+    const int row = j / G::CPR;            // row within the block
+    const int c = j % G::CPR;              // logical 16-byte chunk
+    const int r = kBlock * wq + row;       // row within the tile
+    o.g[i] = (vhalf ? kBlock + row : row) * row_bytes + 16 * c;
+    o.s[i] = r * G::ROWB + 16 * (vhalf ? v_chunk<D>(r, c) : k_chunk<D>(r, c));
+  }
+  return o;
+}
+
+// Load this wave's block of tile t into registers; rows at or past L and
+// blocks outside the pool become zeros (never loaded).
+template <int D>
+__device__ __forceinline__ void fetch(Stage<D>& st, const PrefillParams& p, const BtWindow& bw,
+                                      int t, int L, int g, int wq, int lane, const StageOff& so,
+                                      uint32_t& bad) {
+  using G = Geo<D>;
+  const int key0 = kKeys * t + kBlock * wq;
   const bool exists = key0 < L;
-  const int bid = exists ? bt_row[blk] : -1;
+  const int bid = exists ? bw.get(4 * t + wq) : -1;
   const bool ok = exists && bid >= 0 && (int64_t)bid < p.num_blocks;
   if (exists && !ok) bad = 1;
-  const int64_t row_elems = (int64_t)p.hkv * D;
-  const uint16_t* base = p.cache + (ok ? (int64_t)bid * 2 * kBlock * row_elems : 0) +
-                         (int64_t)(r0 % kBlock) * row_elems + (int64_t)g * D;
-  const uint16_t* zero = reinterpret_cast<const uint16_t*>(p.hdr->zeros);
+  const int64_t row_bytes = (int64_t)p.hkv * D * 2;
+  const char* base = reinterpret_cast<const char*>(p.cache) +
+                     (ok ? (int64_t)bid * 2 * kBlock * row_bytes : 0) + (int64_t)g * D * 2;
 #pragma unroll
-  for (int i = 0; i < G::LPW; ++i) {
-    const int rr = G::RPI * i + lane / G::CPR;   // row among this wave's rows
-    const int r = r0 + rr;                       // row within the tile
-    const int pc = lane % G::CPR;                // chunk this lane fills
-    const bool live = ok && key0 + rr < L;
-    const int dst = (r0 + G::RPI * i) * G::ROWB;
-    const uint16_t* src = VHALF ? base + (kBlock + rr) * row_elems + 8 * v_chunk<D>(r, pc)
-                                : base + rr * row_elems + 8 * k_chunk<D>(r, pc);
-    __builtin_amdgcn_global_load_lds(live ? src : zero, dst_slot + dst, 16, 0, 0);
+  for (int i = 0; i < Stage<D>::NCH; ++i) {
+    const int row = (lane + 64 * i) / G::CPR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok && key0 + row < L) v = *reinterpret_cast<const u32x4*>(base + so.g[i]);
+    st.r[i] = v;
   }
+}
+
+template <int D>
+__device__ __forceinline__ void stash(const Stage<D>& st, const StageOff& so, PKV_LDS char* slot) {
+#pragma unroll
+  for (int i = 0; i < Stage<D>::NCH; ++i) *reinterpret_cast<PKV_LDS u32x4*>(slot + so.s[i]) = st.r[i];
 }
 
 // Order of a matrix phase: a few LDS reads ahead, then one MFMA per read
@@ -180,6 +225,17 @@ __device__ __forceinline__ void qk(f32x16 (&s)[2], const u32x4 (&q)[Geo<D>::NSL]
   pipe_order<2 * G::NSL, 1, 3>();
 }
 
+// Scale O by alpha in the lanes whose maximum moved (a divergent branch:
+// the multiplies run in place under the exec mask and are skipped when no
+// lane of the wave needs them).
+template <int D>
+__device__ __forceinline__ void rescale_o(f32x16 (&o)[Geo<D>::NDT], float alpha) {
+  if (alpha != 1.f) {
+#pragma unroll
+    for (int dt = 0; dt < Geo<D>::NDT; ++dt) o[dt] *= alpha;
+  }
+}
+
 // O^T += V^T P^T over the V tile `vt_lds`.
 template <int D>
 __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2][2],
@@ -204,11 +260,12 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2
 }
 
 // Online softmax of one tile's scores (keys k0 ..): updates the lazy maximum
-// and the row sum, rescales O when the maximum moved, and packs P as the
-// bf16 B operands of PV.  With MASK, keys past lim (per lane) are dropped.
+// and the row sum, sets alpha (the factor O must be scaled by before the
+// next PV: 1 unless the lane's maximum moved) and packs P as the bf16 B
+// operands of PV.  With MASK, keys past lim (per lane) are dropped.
 template <int D, bool MASK>
-__device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], f32x16 (&o)[Geo<D>::NDT],
-                                        float& m, float& l, float c, int k0, int lim, int lane) {
+__device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], float& alpha, float& m,
+                                        float& l, float c, int k0, int lim, int lane) {
   const int h = lane >> 5;
   constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 (1, 1)
   if constexpr (MASK) {
@@ -231,14 +288,11 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], f32x1
   mx = halves_max(mx);
   const bool first = m == -INFINITY;
   const bool upd = first || (mx - m) * c > kLazyMax;
-  if (__builtin_amdgcn_ballot_w64(upd)) {
-    const float mn = upd ? mx : m;
-    const float alpha = first ? 0.f : (upd ? fast_exp2((m - mn) * c) : 1.f);
-    m = mn;
-    l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < Geo<D>::NDT; ++dt) o[dt] *= alpha;
-  }
+  // O is rescaled by alpha right before the next PV (rescale_o), so the
+  // softmax variants never touch the accumulators
+  alpha = upd ? (first ? 0.f : fast_exp2((m - mx) * c)) : 1.f;
+  l *= alpha;
+  m = upd ? mx : m;
   const float mc = m * c;
   float ls = 0.f;
 #pragma unroll
@@ -262,6 +316,7 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], f32x1
 template <int D>
 struct Item {
   const int32_t* bt_row;
+  int nblk;    // ceil(L / 16): entries of the block table in use
   int L, n, h, g, head, qw, ntiles, kfull, kend, lim, qi;
   bool active;
 };
@@ -277,34 +332,40 @@ struct Slots {
 // One tile step t (PAR = t % 2) of one wave: QK(t) and PV(t-1) on the
 // matrix cores, a barrier, the softmax of tile t, a barrier.  Group B runs
 // the same sequence one phase later (it passes one extra barrier first), so
-// each SIMD pairs one wave's matrix phase with the other's softmax.  Group A
-// copies K(t+1) and V(t) at the start of its step and waits for them at the
-// end: the first readers of K(t+1) and V(t) come after that barrier, and the
-// slots they overwrite were last read by group B before the step began.
+// each SIMD pairs one wave's matrix phase with the other's softmax.
+// Copies run two tiles ahead through two register sets: at step t group A
+// loads K(t+2) into set PAR and writes K(t+1) (loaded a step earlier, set
+// 1-PAR) to LDS when the step ends; group B does the same for V in its step
+// t, which ends a phase later.  The slot written was last read by a phase
+// both groups have finished, and its first reader comes after the writer's
+// closing barrier.
 template <int D, int PAR>
 __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>& it, const Slots<D>& sl,
                                           int t, bool group_b, int wave, int lane,
                                           const u32x4 (&q)[Geo<D>::NSL], f32x16 (&o)[Geo<D>::NDT],
-                                          f32x16 (&sc)[2], u32x4 (&pr)[2][2], float& m, float& l,
-                                          const uint32_t (&ak)[Geo<D>::NSL],
-                                          const uint32_t (&av)[Geo<D>::NDT], uint32_t& bad) {
-  if (!group_b) {
-    if (t + 1 < it.ntiles)
-      load_rows<D, false>(p, it.bt_row, t + 1, it.L, it.g, wave, lane, sl.k[1 - PAR], bad);
-    if (t < it.ntiles) load_rows<D, true>(p, it.bt_row, t, it.L, it.g, wave, lane, sl.v[PAR], bad);
+                                          f32x16 (&sc)[2], u32x4 (&pr)[2][2], float& alpha, float& m,
+                                          float& l, const uint32_t (&ak)[Geo<D>::NSL],
+                                          const uint32_t (&av)[Geo<D>::NDT], const StageOff& so,
+                                          Stage<D> (&st)[2], BtWindow& bw, uint32_t& bad) {
+  if (t + 2 < it.ntiles) {
+    if (4 * t + 11 >= bw.base + 64) bw.load(it.bt_row, 4 * t + 8, it.nblk, lane);   // every 16 tiles
+    fetch<D>(st[PAR], p, bw, t + 2, it.L, it.g, wave & 3, lane, so, bad);
   }
   // tile t for QK / softmax, tile t - 1 for PV; tiles no query of the wave sees are skipped
   const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
   const bool do_prev = it.active && t >= 1 && kKeys * (t - 1) < it.kend;
   if (do_t) qk<D>(sc, q, ak, sl.k[PAR]);
-  if (do_prev) pv<D>(o, pr, av, sl.v[1 - PAR]);
+  if (do_prev) {
+    rescale_o<D>(o, alpha);
+    pv<D>(o, pr, av, sl.v[1 - PAR]);
+  }
   wg_barrier();
   if (do_t) {
-    if (kKeys * t + kKeys > it.kfull) softmax<D, true>(sc, pr, o, m, l, p.c, kKeys * t, it.lim, lane);
-    else softmax<D, false>(sc, pr, o, m, l, p.c, kKeys * t, it.lim, lane);
+    if (kKeys * t + kKeys > it.kfull) softmax<D, true>(sc, pr, alpha, m, l, p.c, kKeys * t, it.lim, lane);
+    else softmax<D, false>(sc, pr, alpha, m, l, p.c, kKeys * t, it.lim, lane);
   }
-  if (!group_b) wait_copies();
-  wg_barrier();
+  if (t + 1 < it.ntiles) stash<D>(st[1 - PAR], so, group_b ? sl.v[1 - PAR] : sl.k[1 - PAR]);
+  __syncthreads();
 }
 
 template <int D>
@@ -343,6 +404,8 @@ prefill_kernel(PrefillParams p) {
     }
   }
 
+  const StageOff so = stage_offsets<D>(group_b, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
+
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&p.hdr->prefill_next[queue], 1);
     __syncthreads();
@@ -368,6 +431,7 @@ prefill_kernel(PrefillParams p) {
     it.kfull = it.h + it.qw + 1;                                  // keys all its queries see
     it.kend = it.h + min(it.n - 1, it.qw + 31) + 1;               // keys some query sees
     it.bt_row = p.bt + (int64_t)s * p.width;
+    it.nblk = (it.L + kBlock - 1) / kBlock;
     it.qi = it.qw + (lane & 31);
     it.lim = it.h + it.qi;
     uint32_t bad = 0;
@@ -386,17 +450,22 @@ prefill_kernel(PrefillParams p) {
     f32x16 o[G::NDT];
 #pragma unroll
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f, alpha = 1.f;
     f32x16 sc[2];
     u32x4 pr[2][2];
 
-    if (!group_b) load_rows<D, false>(p, it.bt_row, 0, it.L, it.g, wave, lane, sl.k[0], bad);
-    __syncthreads();   // K(0) in LDS; every wave done with the previous item's slots
+    BtWindow bw;
+    bw.load(it.bt_row, 0, it.nblk, lane);
+    Stage<D> st[2];   // K by group A, V by group B: tile 0 now, tile 1 in flight
+    fetch<D>(st[0], p, bw, 0, it.L, it.g, wave & 3, lane, so, bad);
+    if (1 < it.ntiles) fetch<D>(st[1], p, bw, 1, it.L, it.g, wave & 3, lane, so, bad);
+    stash<D>(st[0], so, group_b ? sl.v[0] : sl.k[0]);
+    __syncthreads();   // K(0) and V(0) in LDS
     if (group_b) wg_barrier();
     for (int t = 0; t <= it.ntiles; t += 2) {
-      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, m, l, ak, av, bad);
+      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, so, st, bw, bad);
       if (t + 1 <= it.ntiles)
-        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, m, l, ak, av, bad);
+        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, so, st, bw, bad);
     }
     if (!group_b) wg_barrier();
     if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
