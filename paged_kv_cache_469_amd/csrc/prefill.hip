@@ -113,85 +113,98 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A window of 64 consecutive block-table entries of the item, one per lane,
-// read with a vector load (so the tile loop issues no scalar memory loads,
-// which would force every LDS wait in it to drain the whole lgkm counter).
-struct BtWindow {
-  int base;    // first block of the window
-  int val;     // this lane's entry: block base + lane, or -1 past the table end
-  __device__ __forceinline__ void load(const int32_t* bt_row, int first, int nblk, int lane) {
-    base = first;
-    val = first + lane < nblk ? bt_row[first + lane] : -1;
-  }
-  // entry of block blk; blk - base must be in [0, 64)
-  __device__ __forceinline__ int get(int blk) const {
-    return __builtin_amdgcn_readlane(val, blk - base);
-  }
-};
+// Block id of block blk of the item, read with a scalar load: the table is
+// not written while the kernel runs, so it can be read through the constant
+// address space.  blk is clamped into the table; the caller ignores the id of
+// a block it does not need.
+using const_i32_ptr = const __attribute__((address_space(4))) int32_t*;
+__device__ __forceinline__ int block_id(const int32_t* bt_row, int blk, int nblk) {
+  return ((const_i32_ptr)bt_row)[min(blk, nblk - 1)];
+}
 
-// Register-staged copy of one 16-key block: group A's wave w stages K of
-// block 4t + w, group B's wave 4 + w stages V of that block, NCH 16-byte
-// chunks per lane, and writes them into the swizzled LDS rows 16w .. 16w+15.
-// (Copying straight from global memory into LDS would leave a copy in
-// flight while the same wave reads its operands from LDS, and the compiler
-// then has to drain every LDS read before each use.)
+// Fourth word of a raw buffer descriptor on gfx950 (32-bit data, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Copy of one 16-key block straight from global memory into LDS: group A's
+// wave w copies K of block 4t + w of a tile, group B's wave 4 + w copies V of
+// that block, into the swizzled LDS rows 16w .. 16w+15 of the tile's slot.
+// Each buffer_load_dwordx4 ... lds writes lane i's 16 bytes at M0 + 16 i, so
+// lane i reads the global chunk that belongs at that LDS position.  The
+// buffer range ends at the last key the item needs: rows past it, and every
+// row of a block outside the pool, arrive as zeros (the range check of a raw
+// buffer access returns zeros), without a branch.  The copies are issued as
+// inline asm and waited for explicitly (copies_landed) before the barrier
+// that hands the slot to its readers; the compiler, not knowing of them,
+// adds no waits of its own to the LDS reads in between.
 template <int D>
-struct Stage {
-  static constexpr int NCH = kBlock * Geo<D>::CPR / 64;
-  u32x4 r[NCH];
-};
-
-// Per-lane byte offsets of the staged chunks: g into the block (from the
-// start of its K half), s into the LDS slot.
-struct StageOff {
-  uint32_t g[4], s[4];
+struct CopyOff {
+  static constexpr int NCH = kBlock * Geo<D>::CPR / 64;   // copies per block
+  uint32_t g[NCH];                                        // per-lane byte offsets into the block half
 };
 
 template <int D>
-__device__ __forceinline__ StageOff stage_offsets(bool vhalf, int wq, int lane, uint32_t row_bytes) {
+__device__ __forceinline__ CopyOff<D> copy_offsets(bool vhalf, int wq, int lane, uint32_t row_bytes) {
   using G = Geo<D>;
-  static_assert(Stage<D>::NCH <= 4, "chunks per lane");
-  StageOff o;
+  CopyOff<D> o;
 #pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
-    const int j = lane + 64 * i;
+  for (int i = 0; i < CopyOff<D>::NCH; ++i) {
+    const int j = lane + 64 * i;           // 16-byte position in the wave's rows
     const int row = j / G::CPR;            // row within the block
-    const int c = j % G::CPR;              // logical 16-byte chunk
+    const int pc = j % G::CPR;             // chunk position within the LDS row
     const int r = kBlock * wq + row;       // row within the tile
-    o.g[i] = (vhalf ? kBlock + row : row) * row_bytes + 16 * c;
-    o.s[i] = r * G::ROWB + 16 * (vhalf ? v_chunk<D>(r, c) : k_chunk<D>(r, c));
+    // both swizzles are involutions: position pc holds chunk swizzle(r, pc)
+    const int c = vhalf ? v_chunk<D>(r, pc) : k_chunk<D>(r, pc);
+    o.g[i] = row * row_bytes + 16 * c;
   }
   return o;
 }
 
-// Load this wave's block of tile t into registers; rows at or past L and
-// blocks outside the pool become zeros (never loaded).
+// Copy this wave's block (id bid, first key key0) of a tile into LDS at
+// lds_dst.  Keys at or past kend (one past the item's last needed key) and
+// every key of a block outside the pool arrive as zeros; a block outside the
+// pool that holds needed keys sets bad.
 template <int D>
-__device__ __forceinline__ void fetch(Stage<D>& st, const PrefillParams& p, const BtWindow& bw,
-                                      int t, int L, int g, int wq, int lane, const StageOff& so,
-                                      uint32_t& bad) {
-  using G = Geo<D>;
-  const int key0 = kKeys * t + kBlock * wq;
-  const bool exists = key0 < L;
-  const int bid = exists ? bw.get(4 * t + wq) : -1;
-  const bool ok = exists && bid >= 0 && (int64_t)bid < p.num_blocks;
-  if (exists && !ok) bad = 1;
+__device__ __forceinline__ void copy_block(const PrefillParams& p, int bid, int key0, int kend,
+                                           int g, bool vhalf, const CopyOff<D>& co,
+                                           uint32_t lds_dst, uint32_t& bad) {
+  const int nvalid = min(max(kend - key0, 0), kBlock);
+  const bool ok = bid >= 0 && (int64_t)bid < p.num_blocks;
+  if (nvalid > 0 && !ok) bad = 1;
   const int64_t row_bytes = (int64_t)p.hkv * D * 2;
-  const char* base = reinterpret_cast<const char*>(p.cache) +
-                     (ok ? (int64_t)bid * 2 * kBlock * row_bytes : 0) + (int64_t)g * D * 2;
-#pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) {
-    const int row = (lane + 64 * i) / G::CPR;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok && key0 + row < L) v = *reinterpret_cast<const u32x4*>(base + so.g[i]);
-    st.r[i] = v;
+  const uint64_t base = reinterpret_cast<uint64_t>(p.cache) +
+                        (ok ? (uint64_t)bid * 2 * kBlock * row_bytes : 0) +
+                        (vhalf ? kBlock * row_bytes : 0) + (uint64_t)g * D * 2;
+  // every field is wave-uniform; readfirstlane keeps the descriptor in SGPRs
+  const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)((base >> 32) & 0xffffu)),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(ok ? (int)(nvalid * row_bytes) : 0),
+                    (uint32_t)kRsrcWord3};
+  // one asm block: copy i lands 1 KiB after copy i-1 (M0 steps by 0x400;
+  // an M0 write needs one wait state before the copy that uses it)
+  if constexpr (CopyOff<D>::NCH == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
+        :: "s"(lds_dst), "v"(co.g[0]), "v"(co.g[1]), "v"(co.g[2]), "v"(co.g[3]), "s"(rs)
+        : "memory", "scc");
+  } else {
+    static_assert(CopyOff<D>::NCH == 2, "copies per block");
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+        :: "s"(lds_dst), "v"(co.g[0]), "v"(co.g[1]), "s"(rs) : "memory", "scc");
   }
 }
 
-template <int D>
-__device__ __forceinline__ void stash(const Stage<D>& st, const StageOff& so, PKV_LDS char* slot) {
-#pragma unroll
-  for (int i = 0; i < Stage<D>::NCH; ++i) *reinterpret_cast<PKV_LDS u32x4*>(slot + so.s[i]) = st.r[i];
+// Wait until this wave's copies have landed in LDS (vmcnt(0)).
+__device__ __forceinline__ void copies_landed() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const PKV_LDS char* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
 // Order of a matrix phase: a few LDS reads ahead, then one MFMA per read
@@ -317,7 +330,7 @@ template <int D>
 struct Item {
   const int32_t* bt_row;
   int nblk;    // ceil(L / 16): entries of the block table in use
-  int L, n, h, g, head, qw, ntiles, kfull, kend, lim, qi;
+  int L, n, h, g, head, qw, kmax, ntiles, kfull, kend, lim, qi;
   bool active;
 };
 
@@ -333,24 +346,31 @@ struct Slots {
 // matrix cores, a barrier, the softmax of tile t, a barrier.  Group B runs
 // the same sequence one phase later (it passes one extra barrier first), so
 // each SIMD pairs one wave's matrix phase with the other's softmax.
-// Copies run two tiles ahead through two register sets: at step t group A
-// loads K(t+2) into set PAR and writes K(t+1) (loaded a step earlier, set
-// 1-PAR) to LDS when the step ends; group B does the same for V in its step
-// t, which ends a phase later.  The slot written was last read by a phase
-// both groups have finished, and its first reader comes after the writer's
-// closing barrier.
+// Copies run one tile ahead into the second slot of K and of V:
+//   group A copies K(t+1) into the K slot of K(t-1) when its step t starts,
+//     and waits for it before its closing barrier;
+//   group B copies V(t+1) into the V slot of V(t-1) when its softmax of
+//     step t starts, and waits for it before its next matrix phase ends.
+// In both cases the slot's last readers (both groups' products of tile t-1)
+// are past a barrier every copying wave has also passed, and the first
+// reader of the new tile comes after the barrier the copying waves reach
+// only once their copies have landed.  The block id a copy needs is read with
+// a scalar load during the step before, where the closing barrier's wait
+// covers it.
 template <int D, int PAR>
 __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>& it, const Slots<D>& sl,
                                           int t, bool group_b, int wave, int lane,
                                           const u32x4 (&q)[Geo<D>::NSL], f32x16 (&o)[Geo<D>::NDT],
                                           f32x16 (&sc)[2], u32x4 (&pr)[2][2], float& alpha, float& m,
                                           float& l, const uint32_t (&ak)[Geo<D>::NSL],
-                                          const uint32_t (&av)[Geo<D>::NDT], const StageOff& so,
-                                          Stage<D> (&st)[2], BtWindow& bw, uint32_t& bad) {
-  if (t + 2 < it.ntiles) {
-    if (4 * t + 11 >= bw.base + 64) bw.load(it.bt_row, 4 * t + 8, it.nblk, lane);   // every 16 tiles
-    fetch<D>(st[PAR], p, bw, t + 2, it.L, it.g, wave & 3, lane, so, bad);
-  }
+                                          const uint32_t (&av)[Geo<D>::NDT], const CopyOff<D>& co,
+                                          int& bid_next, uint32_t& bad) {
+  constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
+  const int wq = wave & 3;
+  const bool copy = t + 1 < it.ntiles;
+  const int key0 = kKeys * (t + 1) + kBlock * wq;            // first key of the block copied
+  if (!group_b && copy)
+    copy_block<D>(p, bid_next, key0, it.kmax, it.g, false, co, lds_addr(sl.k[1 - PAR]) + wq * kBlockBytes, bad);
   // tile t for QK / softmax, tile t - 1 for PV; tiles no query of the wave sees are skipped
   const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
   const bool do_prev = it.active && t >= 1 && kKeys * (t - 1) < it.kend;
@@ -359,12 +379,16 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
     rescale_o<D>(o, alpha);
     pv<D>(o, pr, av, sl.v[1 - PAR]);
   }
+  if (group_b) copies_landed();   // V(t), copied during the step before
   wg_barrier();
+  if (group_b && copy)
+    copy_block<D>(p, bid_next, key0, it.kmax, it.g, true, co, lds_addr(sl.v[1 - PAR]) + wq * kBlockBytes, bad);
+  bid_next = block_id(it.bt_row, 4 * (t + 2) + wq, it.nblk);
   if (do_t) {
     if (kKeys * t + kKeys > it.kfull) softmax<D, true>(sc, pr, alpha, m, l, p.c, kKeys * t, it.lim, lane);
     else softmax<D, false>(sc, pr, alpha, m, l, p.c, kKeys * t, it.lim, lane);
   }
-  if (t + 1 < it.ntiles) stash<D>(st[1 - PAR], so, group_b ? sl.v[1 - PAR] : sl.k[1 - PAR]);
+  if (!group_b) copies_landed();  // K(t+1)
   __syncthreads();
 }
 
@@ -404,7 +428,7 @@ prefill_kernel(PrefillParams p) {
     }
   }
 
-  const StageOff so = stage_offsets<D>(group_b, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
+  const CopyOff<D> co = copy_offsets<D>(group_b, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
 
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&p.hdr->prefill_next[queue], 1);
@@ -425,8 +449,8 @@ prefill_kernel(PrefillParams p) {
     it.h = it.L - it.n;
     it.head = it.g * p.group + hc * hw + wave % hw;
     it.qw = qt * p.query_tile + (wave / hw) * 32;                 // first query of this wave
-    const int kmax = it.h + min(it.n, (qt + 1) * p.query_tile);   // keys the item needs
-    it.ntiles = (kmax + kKeys - 1) / kKeys;
+    it.kmax = it.h + min(it.n, (qt + 1) * p.query_tile);          // keys the item needs
+    it.ntiles = (it.kmax + kKeys - 1) / kKeys;
     it.active = it.qw < it.n;                                     // wave has real queries
     it.kfull = it.h + it.qw + 1;                                  // keys all its queries see
     it.kend = it.h + min(it.n - 1, it.qw + 31) + 1;               // keys some query sees
@@ -454,18 +478,18 @@ prefill_kernel(PrefillParams p) {
     f32x16 sc[2];
     u32x4 pr[2][2];
 
-    BtWindow bw;
-    bw.load(it.bt_row, 0, it.nblk, lane);
-    Stage<D> st[2];   // K by group A, V by group B: tile 0 now, tile 1 in flight
-    fetch<D>(st[0], p, bw, 0, it.L, it.g, wave & 3, lane, so, bad);
-    if (1 < it.ntiles) fetch<D>(st[1], p, bw, 1, it.L, it.g, wave & 3, lane, so, bad);
-    stash<D>(st[0], so, group_b ? sl.v[0] : sl.k[0]);
+    // tile 0: K by group A, V by group B, one block per wave
+    const int wq = wave & 3;
+    copy_block<D>(p, block_id(it.bt_row, wq, it.nblk), kBlock * wq, it.kmax, it.g, group_b, co,
+                  lds_addr(group_b ? sl.v[0] : sl.k[0]) + wq * kBlock * G::ROWB, bad);
+    int bid_next = block_id(it.bt_row, 4 + wq, it.nblk);
+    copies_landed();
     __syncthreads();   // K(0) and V(0) in LDS
     if (group_b) wg_barrier();
     for (int t = 0; t <= it.ntiles; t += 2) {
-      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, so, st, bw, bad);
+      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, co, bid_next, bad);
       if (t + 1 <= it.ntiles)
-        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, so, st, bw, bad);
+        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, co, bid_next, bad);
     }
     if (!group_b) wg_barrier();
     if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
