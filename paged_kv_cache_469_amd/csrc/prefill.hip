@@ -198,9 +198,11 @@ __device__ __forceinline__ void copy_block(const PrefillParams& p, int bid, int 
   }
 }
 
-// Wait until this wave's copies have landed in LDS (vmcnt(0)).
+// Wait until all but the last N of this wave's copies have landed in LDS
+// (the wave issues no other vector memory operations meanwhile).
+template <int N>
 __device__ __forceinline__ void copies_landed() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const PKV_LDS char* p) {
@@ -209,8 +211,9 @@ __device__ __forceinline__ uint32_t lds_addr(const PKV_LDS char* p) {
 
 // Order of a matrix phase: a few LDS reads ahead, then one MFMA per read
 // (two reads per MFMA for the transposed V operand), so only a handful of
-// operand fragments are live at a time.
-template <int MFMAS, int READS, int LEAD>
+// operand fragments are live at a time; VALU independent vector
+// instructions go after each MFMA, where they issue while it runs.
+template <int MFMAS, int READS, int LEAD, int VALU = 0>
 __device__ __forceinline__ void pipe_order() {
 #pragma unroll
   for (int i = 0; i < LEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
@@ -218,11 +221,12 @@ __device__ __forceinline__ void pipe_order() {
   for (int i = 0; i < MFMAS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i + LEAD < MFMAS) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
   }
 }
 
 // S^T of this wave's 32 queries over the two 32-key halves of the K tile `kt_lds`.
-template <int D>
+template <int D, int VALU = 0>
 __device__ __forceinline__ void qk(f32x16 (&s)[2], const u32x4 (&q)[Geo<D>::NSL],
                                    const uint32_t (&ak)[Geo<D>::NSL], const PKV_LDS char* kt_lds) {
   using G = Geo<D>;
@@ -235,7 +239,7 @@ __device__ __forceinline__ void qk(f32x16 (&s)[2], const u32x4 (&q)[Geo<D>::NSL]
       s[kt] = mfma32(k, q[sl], sl == 0 ? f32x16{} : s[kt]);
     }
   }
-  pipe_order<2 * G::NSL, 1, 3>();
+  pipe_order<2 * G::NSL, 1, 3, VALU>();
 }
 
 // Scale O by alpha in the lanes whose maximum moved (a divergent branch:
@@ -250,7 +254,7 @@ __device__ __forceinline__ void rescale_o(f32x16 (&o)[Geo<D>::NDT], float alpha)
 }
 
 // O^T += V^T P^T over the V tile `vt_lds`.
-template <int D>
+template <int D, int VALU = 0>
 __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2][2],
                                    const uint32_t (&av)[Geo<D>::NDT], const PKV_LDS char* vt_lds) {
   using G = Geo<D>;
@@ -269,24 +273,25 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2
       }
     }
   }
-  pipe_order<4 * G::NDT, 2, 3>();
+  pipe_order<4 * G::NDT, 2, 3, VALU>();
 }
 
-// Online softmax of one tile's scores (keys k0 ..): updates the lazy maximum
-// and the row sum, sets alpha (the factor O must be scaled by before the
-// next PV: 1 unless the lane's maximum moved) and packs P as the bf16 B
-// operands of PV.  With MASK, keys past lim (per lane) are dropped.
-template <int D, bool MASK>
-__device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], float& alpha, float& m,
-                                        float& l, float c, int k0, int lim, int lane) {
-  const int h = lane >> 5;
-  constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 (1, 1)
+// Online softmax of one tile, in two parts so the matrix phase can take
+// the first:
+//   tile_max  the row maximum of the tile's scores (after dropping keys past
+//             lim in a diagonal tile), both halves of the wave combined;
+//   tile_exp  moves the lazy maximum m, sets alpha (the factor O and l are
+//             scaled by: 1 unless the lane's maximum moved), turns the
+//             scores into P = exp2(S c - m c) (bf16, as the B operands of
+//             PV) and adds their fp32 row sum to l.
+template <bool MASK>
+__device__ __forceinline__ float tile_max(f32x16 (&s)[2], int k0, int lim, int lane) {
   if constexpr (MASK) {
     // key of register r of half kt = k0 + 4h + (32kt + 8(r/4) + r%4); the
     // distance t = lim - key is compared with 0 in float arithmetic: a
     // dropped key gets t * 1e38 <= -1e38 added (-inf for t <= -4), a kept one
     // gets 0.  No lane masks or selects, and the scores are finite, so no NaN.
-    const float fb = (float)(lim - k0 - 4 * h);
+    const float fb = (float)(lim - k0 - 4 * (lane >> 5));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -298,16 +303,18 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], float
   float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-  mx = halves_max(mx);
+  return halves_max(mx);
+}
+
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], float mx, u32x4 (&pr)[2][2],
+                                         float& alpha, float& m, float& l, float c) {
   const bool first = m == -INFINITY;
   const bool upd = first || (mx - m) * c > kLazyMax;
-  // O is rescaled by alpha right before the next PV (rescale_o), so the
-  // softmax variants never touch the accumulators
   alpha = upd ? (first ? 0.f : fast_exp2((m - mx) * c)) : 1.f;
   l *= alpha;
   m = upd ? mx : m;
   const float mc = m * c;
-  float ls = 0.f;
+  float sa = 0.f, sb = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -316,13 +323,16 @@ __device__ __forceinline__ void softmax(f32x16 (&s)[2], u32x4 (&pr)[2][2], float
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 8 * u + 2 * i;
-        w[i] = pack_bf16(fast_exp2(fmaf(s[kt][r], c, -mc)), fast_exp2(fmaf(s[kt][r + 1], c, -mc)));
-        ls = dot2_bf16(w[i], kOnes, ls);
+        const float e0 = fast_exp2(fmaf(s[kt][r], c, -mc));
+        const float e1 = fast_exp2(fmaf(s[kt][r + 1], c, -mc));
+        w[i] = pack_bf16(e0, e1);
+        sa += e0;
+        sb += e1;
       }
       pr[kt][u] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
-  l += ls;
+  l += sa + sb;
 }
 
 // Everything one wave needs for one work item.
@@ -334,61 +344,72 @@ struct Item {
   bool active;
 };
 
-// LDS slots: K and V of two tiles, as four separate objects so the compiler
-// can tell that a copy into one slot never touches the slot being read.
+// LDS slots: K and V of three tiles (tile j in slot j % 3), as separate
+// objects so the compiler can tell that a copy into one slot never touches
+// the slot being read.
 template <int D>
 struct Slots {
-  PKV_LDS char* k[2];
-  PKV_LDS char* v[2];
+  PKV_LDS char* k[3];
+  PKV_LDS char* v[3];
 };
 
-// One tile step t (PAR = t % 2) of one wave: QK(t) and PV(t-1) on the
+// One tile step t (R = t % 3) of one wave: QK(t) and PV(t-1) on the
 // matrix cores, a barrier, the softmax of tile t, a barrier.  Group B runs
 // the same sequence one phase later (it passes one extra barrier first), so
-// each SIMD pairs one wave's matrix phase with the other's softmax.
-// Copies run one tile ahead into the second slot of K and of V:
-//   group A copies K(t+1) into the K slot of K(t-1) when its step t starts,
-//     and waits for it before its closing barrier;
-//   group B copies V(t+1) into the V slot of V(t-1) when its softmax of
-//     step t starts, and waits for it before its next matrix phase ends.
-// In both cases the slot's last readers (both groups' products of tile t-1)
-// are past a barrier every copying wave has also passed, and the first
-// reader of the new tile comes after the barrier the copying waves reach
-// only once their copies have landed.  The block id a copy needs is read with
-// a scalar load during the step before, where the closing barrier's wait
-// covers it.
-template <int D, int PAR>
+// each SIMD pairs one wave's matrix phase with the other's softmax.  With
+// barrier 2t opening group A's step t:
+//   group A: matrix phase (2t, 2t+1], softmax phase (2t+1, 2t+2];
+//   group B: matrix phase (2t+1, 2t+2], softmax phase (2t+2, 2t+3].
+// Copies: when its softmax phase of step t starts, wave w of group A copies
+// block w of K(t+2) into the slot of K(t-1) and block w of V(t+1) into the
+// slot of V(t-2), and waits for them before its closing barrier of step t+1.
+// The slots' last readers (group B's products of step t-1) finished by
+// barrier 2t; the first readers of the new tiles (group A's QK(t+2) and
+// PV(t+1)) start after barrier 2t+4.  The products of both groups between
+// those barriers read the other slots.  Group B copies nothing.
+template <int D, int R>
 __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>& it, const Slots<D>& sl,
                                           int t, bool group_b, int wave, int lane,
                                           const u32x4 (&q)[Geo<D>::NSL], f32x16 (&o)[Geo<D>::NDT],
                                           f32x16 (&sc)[2], u32x4 (&pr)[2][2], float& alpha, float& m,
                                           float& l, const uint32_t (&ak)[Geo<D>::NSL],
-                                          const uint32_t (&av)[Geo<D>::NDT], const CopyOff<D>& co,
-                                          int& bid_next, uint32_t& bad) {
+                                          const uint32_t (&av)[Geo<D>::NDT], const CopyOff<D>& ck,
+                                          const CopyOff<D>& cv, int& bid1, int& bid2, uint32_t& bad) {
+  constexpr int RP = (R + 2) % 3;   // slot of tiles t - 1 and t + 2
+  constexpr int RN = (R + 1) % 3;   // slot of tiles t + 1 and t - 2
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
   const int wq = wave & 3;
-  const bool copy = t + 1 < it.ntiles;
-  const int key0 = kKeys * (t + 1) + kBlock * wq;            // first key of the block copied
-  if (!group_b && copy)
-    copy_block<D>(p, bid_next, key0, it.kmax, it.g, false, co, lds_addr(sl.k[1 - PAR]) + wq * kBlockBytes, bad);
-  // tile t for QK / softmax, tile t - 1 for PV; tiles no query of the wave sees are skipped
-  const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
-  const bool do_prev = it.active && t >= 1 && kKeys * (t - 1) < it.kend;
-  if (do_t) qk<D>(sc, q, ak, sl.k[PAR]);
-  if (do_prev) {
-    rescale_o<D>(o, alpha);
-    pv<D>(o, pr, av, sl.v[1 - PAR]);
-  }
-  if (group_b) copies_landed();   // V(t), copied during the step before
+  // Matrix phase: QK(t) and PV(t-1) run on every step, as one scheduling
+  // region.  A tile the wave does not use (before the first, past the last,
+  // or past every key its queries see) has P = 0, and every slot read holds
+  // finite values, so the extra products change nothing.
+  qk<D>(sc, q, ak, sl.k[R]);
+  pv<D>(o, pr, av, sl.v[RP]);
   wg_barrier();
-  if (group_b && copy)
-    copy_block<D>(p, bid_next, key0, it.kmax, it.g, true, co, lds_addr(sl.v[1 - PAR]) + wq * kBlockBytes, bad);
-  bid_next = block_id(it.bt_row, 4 * (t + 2) + wq, it.nblk);
-  if (do_t) {
-    if (kKeys * t + kKeys > it.kfull) softmax<D, true>(sc, pr, alpha, m, l, p.c, kKeys * t, it.lim, lane);
-    else softmax<D, false>(sc, pr, alpha, m, l, p.c, kKeys * t, it.lim, lane);
+  if (!group_b) {
+    copy_block<D>(p, bid2, kKeys * (t + 2) + kBlock * wq, it.kmax, it.g, false, ck,
+                  lds_addr(sl.k[RP]) + wq * kBlockBytes, bad);
+    copy_block<D>(p, bid1, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
+                  lds_addr(sl.v[RN]) + wq * kBlockBytes, bad);
+    bid1 = bid2;                                          // block of tile t + 2
+    bid2 = block_id(it.bt_row, 4 * (t + 3) + wq, it.nblk);
   }
-  if (!group_b) copies_landed();  // K(t+1)
+  // tile t for the softmax; tiles no query of the wave sees are skipped
+  const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
+  if (do_t) {
+    // a diagonal tile (some query of the wave drops keys of it) is masked
+    const float mx = kKeys * t + kKeys > it.kfull ? tile_max<true>(sc, kKeys * t, it.lim, lane)
+                                                  : tile_max<false>(sc, kKeys * t, it.lim, lane);
+    tile_exp(sc, mx, pr, alpha, m, l, p.c);
+    rescale_o<D>(o, alpha);   // O is scaled before the next PV adds tile t
+  } else {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // group A: the copies of the step before have landed (this step's may not)
+  if (!group_b) copies_landed<2 * CopyOff<D>::NCH>();
   __syncthreads();
 }
 
@@ -398,11 +419,13 @@ prefill_kernel(PrefillParams p) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(1024))) char k0_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char k1_lds[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k2_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char v0_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char v1_lds[G::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v2_lds[G::TILEB];
   __shared__ int s_item;
-  const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds},
-                       {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds}};
+  const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds, (PKV_LDS char*)k2_lds},
+                       {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds, (PKV_LDS char*)v2_lds}};
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -428,7 +451,8 @@ prefill_kernel(PrefillParams p) {
     }
   }
 
-  const CopyOff<D> co = copy_offsets<D>(group_b, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
+  const CopyOff<D> ck = copy_offsets<D>(false, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
+  const CopyOff<D> cv = copy_offsets<D>(true, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
 
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(&p.hdr->prefill_next[queue], 1);
@@ -476,21 +500,40 @@ prefill_kernel(PrefillParams p) {
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x16{};
     float m = -INFINITY, l = 0.f, alpha = 1.f;
     f32x16 sc[2];
-    u32x4 pr[2][2];
+    u32x4 pr[2][2];   // P of the tile before the first: zero
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
+    // the first step multiplies that zero P by the V slot of tile -1, which
+    // must hold finite values: clear it (every wave is past the last item's reads)
+    for (int i = threadIdx.x; i < G::TILEB / 16; i += kWaves * 64)
+      reinterpret_cast<PKV_LDS u32x4*>(sl.v[2])[i] = u32x4{0u, 0u, 0u, 0u};
 
-    // tile 0: K by group A, V by group B, one block per wave
+    // K(0) and K(1) by group A, V(0) by group B, one block per wave each
     const int wq = wave & 3;
-    copy_block<D>(p, block_id(it.bt_row, wq, it.nblk), kBlock * wq, it.kmax, it.g, group_b, co,
-                  lds_addr(group_b ? sl.v[0] : sl.k[0]) + wq * kBlock * G::ROWB, bad);
-    int bid_next = block_id(it.bt_row, 4 + wq, it.nblk);
-    copies_landed();
-    __syncthreads();   // K(0) and V(0) in LDS
-    if (group_b) wg_barrier();
-    for (int t = 0; t <= it.ntiles; t += 2) {
-      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, co, bid_next, bad);
-      if (t + 1 <= it.ntiles)
-        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, co, bid_next, bad);
+    int bid1 = block_id(it.bt_row, 4 + wq, it.nblk);   // block of tile 1
+    int bid2 = block_id(it.bt_row, 8 + wq, it.nblk);   // block of tile 2
+    if (!group_b) {
+      copy_block<D>(p, block_id(it.bt_row, wq, it.nblk), kBlock * wq, it.kmax, it.g, false, ck,
+                    lds_addr(sl.k[0]) + wq * kBlock * G::ROWB, bad);
+      copy_block<D>(p, bid1, kKeys + kBlock * wq, it.kmax, it.g, false, ck,
+                    lds_addr(sl.k[1]) + wq * kBlock * G::ROWB, bad);
+    } else {
+      copy_block<D>(p, block_id(it.bt_row, wq, it.nblk), kBlock * wq, it.kmax, it.g, true, cv,
+                    lds_addr(sl.v[0]) + wq * kBlock * G::ROWB, bad);
     }
+    copies_landed<0>();
+    __syncthreads();   // K(0), K(1), V(0) in LDS, the V slot of tile -1 cleared
+    if (group_b) wg_barrier();
+    for (int t = 0; t <= it.ntiles; t += 3) {
+      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, bid1, bid2, bad);
+      if (t + 1 <= it.ntiles)
+        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, bid1, bid2, bad);
+      if (t + 2 <= it.ntiles)
+        tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, bid1, bid2, bad);
+    }
+    if (!group_b) copies_landed<0>();   // nothing in flight into the slots past the item
     if (!group_b) wg_barrier();
     if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
 
