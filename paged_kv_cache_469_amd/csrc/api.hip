@@ -83,7 +83,7 @@ Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int
   l.decode_items = off;
   off = align256(off + (size_t)l.decode_cap * sizeof(int2));
   l.prefill_items = off;
-  off = align256(off + (size_t)l.prefill_cap * sizeof(int2));
+  off = align256(off + (size_t)l.prefill_cap * sizeof(pkv::PrefillItem));
   l.part_ml = off;
   off = align256(off + (size_t)l.decode_cap * hq * sizeof(float2));
   l.part_o = off;
@@ -228,11 +228,13 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   PlanParams pp{};
   pp.cu = cu_seqlens_q;
   pp.lens = seq_lens;
+  pp.bt = block_tables;
   pp.hdr = hdr;
   pp.decode_items = reinterpret_cast<int2*>(ws + l.decode_items);
-  pp.prefill_items = reinterpret_cast<int2*>(ws + l.prefill_items);
+  pp.prefill_items = reinterpret_cast<pkv::PrefillItem*>(ws + l.prefill_items);
   pp.num_seqs = num_seqs;
   pp.num_tokens = num_tokens;
+  pp.width = max_blocks_per_seq;
   pp.max_len = max_blocks_per_seq * kBlock;
   pp.part_tokens = l.part_tokens;
   pp.query_tile = query_tile;

@@ -6,14 +6,29 @@
 
 namespace pkv {
 
+// One prefill work entry as the plan kernel leaves it: the segment, its
+// query tile, and what the attention kernel needs before its first tile
+// (the segment bounds and the block ids of keys 0..127).
+struct PrefillItem {
+  int32_t seq, qt;
+  int32_t L;        // tokens in the sequence
+  int32_t tok0;     // first new token in the packed batch
+  int32_t n;        // new tokens of the segment
+  int32_t pad[3];
+  int32_t bid[8];   // block-table entries 0..7, clamped to the entries in use
+};
+static_assert(sizeof(PrefillItem) == 64, "one scalar load of 16 dwords");
+
 struct PlanParams {
   const int32_t* cu;
   const int32_t* lens;
+  const int32_t* bt;
   WsHeader* hdr;
   int2* decode_items;
-  int2* prefill_items;
+  PrefillItem* prefill_items;
   int32_t num_seqs;
   int32_t num_tokens;
+  int32_t width;         // block-table row length
   int32_t max_len;       // max_blocks_per_seq * 16
   int32_t part_tokens;   // P
   int32_t query_tile;    // QT
@@ -49,7 +64,7 @@ struct PrefillParams {
   const int32_t* lens;
   uint16_t* out;
   WsHeader* hdr;
-  const int2* items;       // (segment, query tile), most key tiles first
+  const PrefillItem* items;   // most key tiles first
   int64_t q_stride;
   int64_t num_blocks;
   int32_t width;

@@ -6,7 +6,8 @@
 // One workgroup of 1024 threads walks the segments on the device, so the
 // host never reads metadata and the whole call can be captured in a graph:
 //   n == 1 -> decode: ceil(L / P) items (segment, partition)
-//   n >  1 -> prefill: ceil(n / QT) items (segment, query tile)
+//   n >  1 -> prefill: ceil(n / QT) items (segment, query tile), each with
+//             the segment bounds and its first eight block ids
 //   n == 0 -> nothing
 // Prefill items are ordered by their number of 64-key tiles, most first (a
 // counting sort over 1024 cost buckets), so the dynamic queues hand out the
@@ -123,9 +124,19 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       const SegInfo si = seg_info(p, s);
       if (si.ok && si.n > 1) {
         const int np = (si.n + p.query_tile - 1) / p.query_tile;
+        PrefillItem it{};
+        it.seq = s;
+        it.L = si.L;
+        it.tok0 = p.cu[s];
+        it.n = si.n;
+        const int32_t* bt_row = p.bt + (int64_t)s * p.width;
+        const int nblk = (si.L + kBlock - 1) / kBlock;   // >= 1: L >= n > 1
+#pragma unroll
+        for (int j = 0; j < 8; ++j) it.bid[j] = bt_row[min(j, nblk - 1)];
         for (int qt = 0; qt < np; ++qt) {
           const int at = atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
-          if (at < p.prefill_cap) p.prefill_items[at] = make_int2(s, qt);
+          it.qt = qt;
+          if (at < p.prefill_cap) p.prefill_items[at] = it;
         }
       }
     }

@@ -113,13 +113,17 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Block id of block blk of the item, read with a scalar load: the table is
-// not written while the kernel runs, so it can be read through the constant
-// address space.  blk is clamped into the table; the caller ignores the id of
-// a block it does not need.
-using const_i32_ptr = const __attribute__((address_space(4))) int32_t*;
-__device__ __forceinline__ int block_id(const int32_t* bt_row, int blk, int nblk) {
-  return ((const_i32_ptr)bt_row)[min(blk, nblk - 1)];
+// The item's block table lives in LDS, in windows of 256 entries (64 tiles),
+// two of them: window w (blocks 256w .. 256w+255, entries past the table
+// clamped to its last one) in slot w % 2.  Group B, which has no copy in
+// flight, loads the windows with vector loads (window 0 when the item
+// starts, window w+1 during step 64w+1, written a step later); group A reads
+// its block ids from them.  So the tile steps issue no scalar loads, which
+// would hold up every LDS wait until they return.
+constexpr int kWindow = 256;
+
+__device__ __forceinline__ int window_entry(const int32_t* bt_row, int w, int wb, int lane, int nblk) {
+  return bt_row[min(kWindow * w + 64 * wb + lane, nblk - 1)];
 }
 
 // Fourth word of a raw buffer descriptor on gfx950 (32-bit data, no swizzle).
@@ -340,9 +344,38 @@ template <int D>
 struct Item {
   const int32_t* bt_row;
   int nblk;    // ceil(L / 16): entries of the block table in use
-  int L, n, h, g, head, qw, kmax, ntiles, kfull, kend, lim, qi;
+  int L, n, h, g, head, qw, kmax, ntiles, kfull, kend, lim, qi, tok0;
   bool active;
 };
+
+// Item itx (descriptor d, in LDS) as this wave sees it.
+template <int D>
+__device__ __forceinline__ Item<D> item_of(const PrefillParams& p, const PrefillItem* d,
+                                           int itx, int per_entry, int queue, int wave, int lane) {
+  const int sub = itx % per_entry;
+  const int hc = sub % p.head_chunks;
+  const int s = __builtin_amdgcn_readfirstlane(d->seq);
+  const int qt = __builtin_amdgcn_readfirstlane(d->qt);
+  const int hw = p.heads_per_item;
+  Item<D> it;
+  it.g = queue + p.num_queues * (sub / p.head_chunks);
+  it.L = __builtin_amdgcn_readfirstlane(d->L);
+  it.tok0 = __builtin_amdgcn_readfirstlane(d->tok0);
+  it.n = __builtin_amdgcn_readfirstlane(d->n);
+  it.h = it.L - it.n;
+  it.head = it.g * p.group + hc * hw + wave % hw;
+  it.qw = qt * p.query_tile + (wave / hw) * 32;                 // first query of this wave
+  it.kmax = it.h + min(it.n, (qt + 1) * p.query_tile);          // keys the item needs
+  it.ntiles = (it.kmax + kKeys - 1) / kKeys;
+  it.active = it.qw < it.n;                                     // wave has real queries
+  it.kfull = it.h + it.qw + 1;                                  // keys all its queries see
+  it.kend = it.h + min(it.n - 1, it.qw + 31) + 1;               // keys some query sees
+  it.bt_row = p.bt + (int64_t)s * p.width;
+  it.nblk = (it.L + kBlock - 1) / kBlock;
+  it.qi = it.qw + (lane & 31);
+  it.lim = it.h + it.qi;
+  return it;
+}
 
 // LDS slots: K and V of three tiles (tile j in slot j % 3), as separate
 // objects so the compiler can tell that a copy into one slot never touches
@@ -374,7 +407,9 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
                                           f32x16 (&sc)[2], u32x4 (&pr)[2][2], float& alpha, float& m,
                                           float& l, const uint32_t (&ak)[Geo<D>::NSL],
                                           const uint32_t (&av)[Geo<D>::NDT], const CopyOff<D>& ck,
-                                          const CopyOff<D>& cv, int& bid1, int& bid2, uint32_t& bad) {
+                                          const CopyOff<D>& cv, int32_t (*bt)[kWindow],
+                                          int& bt_next, uint32_t& bad, int& nxt, int& nxt_word,
+                                          int n_items, int per_entry) {
   constexpr int RP = (R + 2) % 3;   // slot of tiles t - 1 and t + 2
   constexpr int RN = (R + 1) % 3;   // slot of tiles t + 1 and t - 2
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
@@ -387,12 +422,27 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   pv<D>(o, pr, av, sl.v[RP]);
   wg_barrier();
   if (!group_b) {
-    copy_block<D>(p, bid2, kKeys * (t + 2) + kBlock * wq, it.kmax, it.g, false, ck,
+    const int bk = 4 * (t + 2) + wq, bv = 4 * (t + 1) + wq;   // blocks of K(t+2) and V(t+1)
+    const int bid_k = __builtin_amdgcn_readfirstlane(bt[(bk / kWindow) & 1][bk % kWindow]);
+    const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
+    copy_block<D>(p, bid_k, kKeys * (t + 2) + kBlock * wq, it.kmax, it.g, false, ck,
                   lds_addr(sl.k[RP]) + wq * kBlockBytes, bad);
-    copy_block<D>(p, bid1, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
+    copy_block<D>(p, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
                   lds_addr(sl.v[RN]) + wq * kBlockBytes, bad);
-    bid1 = bid2;                                          // block of tile t + 2
-    bid2 = block_id(it.bt_row, 4 * (t + 3) + wq, it.nblk);
+  } else {
+    const int w = t / 64 + 1;   // the window after the current one
+    if ((t & 63) == 1 && kWindow * w < it.nblk) {
+      bt_next = window_entry(it.bt_row, w, wave - kWaves / 2, lane, it.nblk);
+    } else if ((t & 63) == 2 && kWindow * w < it.nblk) {
+      bt[w & 1][64 * (wave - kWaves / 2) + lane] = bt_next;
+    }
+    if (wave == kWaves / 2 && t == 1) {
+      // the next item: its index (asked for when this item started) and its
+      // descriptor, one dword per lane, written to LDS when this item ends
+      nxt = __builtin_amdgcn_readfirstlane(nxt);
+      const int32_t* src = reinterpret_cast<const int32_t*>(p.items + min(nxt, n_items - 1) / per_entry);
+      nxt_word = src[lane & 15];
+    }
   }
   // tile t for the softmax; tiles no query of the wave sees are skipped
   const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
@@ -423,7 +473,9 @@ prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char v0_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char v1_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char v2_lds[G::TILEB];
-  __shared__ int s_item;
+  __shared__ PrefillItem s_desc[2];   // the current and the next item
+  __shared__ int s_itx[2];
+  __shared__ int32_t s_bt[2][kWindow];   // block-table windows of the current item
   const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds, (PKV_LDS char*)k2_lds},
                        {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds, (PKV_LDS char*)v2_lds}};
 
@@ -454,47 +506,60 @@ prefill_kernel(PrefillParams p) {
   const CopyOff<D> ck = copy_offsets<D>(false, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
   const CopyOff<D> cv = copy_offsets<D>(true, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
 
-  for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(&p.hdr->prefill_next[queue], 1);
-    __syncthreads();
-    const int itx = s_item;
-    __syncthreads();
-    if (itx >= n_items) break;
-    const int2 entry = p.items[itx / per_entry];
-    const int sub = itx % per_entry;
-    const int hc = sub % p.head_chunks;
-    const int s = entry.x;
-    const int qt = entry.y;
-    Item<D> it;
-    it.g = queue + p.num_queues * (sub / p.head_chunks);
-    it.L = p.lens[s];
-    const int tok0 = p.cu[s];
-    it.n = p.cu[s + 1] - tok0;
-    it.h = it.L - it.n;
-    it.head = it.g * p.group + hc * hw + wave % hw;
-    it.qw = qt * p.query_tile + (wave / hw) * 32;                 // first query of this wave
-    it.kmax = it.h + min(it.n, (qt + 1) * p.query_tile);          // keys the item needs
-    it.ntiles = (it.kmax + kKeys - 1) / kKeys;
-    it.active = it.qw < it.n;                                     // wave has real queries
-    it.kfull = it.h + it.qw + 1;                                  // keys all its queries see
-    it.kend = it.h + min(it.n - 1, it.qw + 31) + 1;               // keys some query sees
-    it.bt_row = p.bt + (int64_t)s * p.width;
-    it.nblk = (it.L + kBlock - 1) / kBlock;
-    it.qi = it.qw + (lane & 31);
-    it.lim = it.h + it.qi;
-    uint32_t bad = 0;
-
-    u32x4 q[G::NSL];
-    {
-      const uint16_t* qrow =
-          p.q + (int64_t)(tok0 + it.qi) * p.q_stride + (int64_t)it.head * D + 8 * (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < G::NSL; ++i) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (it.qi < it.n) v = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
-        q[i] = v ^ p.q_sign;
-      }
+  // the first item: wave 4 asks for its index and reads its descriptor
+  if (wave == kWaves / 2) {
+    int itx0 = 0;
+    if (lane == 0) itx0 = atomicAdd(&p.hdr->prefill_next[queue], 1);
+    itx0 = __builtin_amdgcn_readfirstlane(itx0);
+    if (lane < 16) {
+      const int32_t* src = reinterpret_cast<const int32_t*>(p.items + min(itx0, n_items - 1) / per_entry);
+      reinterpret_cast<int32_t*>(&s_desc[0])[lane] = src[lane];
     }
+    if (lane == 0) s_itx[0] = itx0;
+  }
+  __syncthreads();
+  int cur = 0;
+  int itx = s_itx[0];
+  if (itx >= n_items) return;
+  Item<D> it = item_of<D>(p, &s_desc[0], itx, per_entry, queue, wave, lane);
+
+  const int wq = wave & 3;
+  u32x4 q[G::NSL];
+  int bt_next = 0;   // group B: a lane's entry of the next block-table window
+  uint32_t bad = 0;
+  // Start of an item: its queries into registers, the V slot of tile -1
+  // cleared (the first step multiplies a zero P by it, so it must hold
+  // finite values), the copies of K(0), K(1) (group A) and V(0) (group B),
+  // one block per wave each, with the block ids from the descriptor, and
+  // (group B) the loads of block-table window 0, written when the item runs.
+  auto start_item = [&](const Item<D>& nx, const PrefillItem* d) {
+    const uint16_t* qrow =
+        p.q + (int64_t)(nx.tok0 + nx.qi) * p.q_stride + (int64_t)nx.head * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < G::NSL; ++i) {   // sign applied once they have arrived
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (nx.qi < nx.n) v = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
+      q[i] = v;
+    }
+    for (int i = threadIdx.x; i < G::TILEB / 16; i += kWaves * 64)
+      reinterpret_cast<PKV_LDS u32x4*>(sl.v[2])[i] = u32x4{0u, 0u, 0u, 0u};
+    const int bid0 = __builtin_amdgcn_readfirstlane(d->bid[wq]);
+    const int bid1 = __builtin_amdgcn_readfirstlane(d->bid[4 + wq]);   // block of tile 1
+    if (group_b) bt_next = window_entry(nx.bt_row, 0, wave - kWaves / 2, lane, nx.nblk);
+    if (!group_b) {
+      copy_block<D>(p, bid0, kBlock * wq, nx.kmax, nx.g, false, ck,
+                    lds_addr(sl.k[0]) + wq * kBlock * G::ROWB, bad);
+      copy_block<D>(p, bid1, kKeys + kBlock * wq, nx.kmax, nx.g, false, ck,
+                    lds_addr(sl.k[1]) + wq * kBlock * G::ROWB, bad);
+    } else {
+      copy_block<D>(p, bid0, kBlock * wq, nx.kmax, nx.g, true, cv,
+                    lds_addr(sl.v[0]) + wq * kBlock * G::ROWB, bad);
+    }
+  };
+  start_item(it, &s_desc[0]);
+
+  for (;;) {
+    int nxt = 0, nxt_word = 0;   // wave 4: the next item's index and descriptor
     f32x16 o[G::NDT];
 #pragma unroll
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x16{};
@@ -505,43 +570,46 @@ prefill_kernel(PrefillParams p) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
-    // the first step multiplies that zero P by the V slot of tile -1, which
-    // must hold finite values: clear it (every wave is past the last item's reads)
-    for (int i = threadIdx.x; i < G::TILEB / 16; i += kWaves * 64)
-      reinterpret_cast<PKV_LDS u32x4*>(sl.v[2])[i] = u32x4{0u, 0u, 0u, 0u};
 
-    // K(0) and K(1) by group A, V(0) by group B, one block per wave each
-    const int wq = wave & 3;
-    int bid1 = block_id(it.bt_row, 4 + wq, it.nblk);   // block of tile 1
-    int bid2 = block_id(it.bt_row, 8 + wq, it.nblk);   // block of tile 2
-    if (!group_b) {
-      copy_block<D>(p, block_id(it.bt_row, wq, it.nblk), kBlock * wq, it.kmax, it.g, false, ck,
-                    lds_addr(sl.k[0]) + wq * kBlock * G::ROWB, bad);
-      copy_block<D>(p, bid1, kKeys + kBlock * wq, it.kmax, it.g, false, ck,
-                    lds_addr(sl.k[1]) + wq * kBlock * G::ROWB, bad);
-    } else {
-      copy_block<D>(p, block_id(it.bt_row, wq, it.nblk), kBlock * wq, it.kmax, it.g, true, cv,
-                    lds_addr(sl.v[0]) + wq * kBlock * G::ROWB, bad);
-    }
-    copies_landed<0>();
-    __syncthreads();   // K(0), K(1), V(0) in LDS, the V slot of tile -1 cleared
+    if (group_b) s_bt[0][64 * (wave - kWaves / 2) + lane] = bt_next;   // window 0
+    copies_landed<0>();   // the copies and the query loads
+    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS, the V slot of tile -1 cleared
+#pragma unroll
+    for (int i = 0; i < G::NSL; ++i) q[i] ^= p.q_sign;
+    // asked for only now, so the wait for the copies above does not include it
+    if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[queue], 1);
     if (group_b) wg_barrier();
     for (int t = 0; t <= it.ntiles; t += 3) {
-      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, bid1, bid2, bad);
+      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
       if (t + 1 <= it.ntiles)
-        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, bid1, bid2, bad);
+        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
       if (t + 2 <= it.ntiles)
-        tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, bid1, bid2, bad);
+        tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
     }
-    if (!group_b) copies_landed<0>();   // nothing in flight into the slots past the item
-    if (!group_b) wg_barrier();
-    if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
+    if (!group_b) {
+      copies_landed<0>();   // nothing in flight into the slots past the item
+      wg_barrier();         // group B's last step ends here
+    }
+    if (wave == kWaves / 2) {
+      if (lane < 16) reinterpret_cast<int32_t*>(&s_desc[cur ^ 1])[lane] = nxt_word;
+      if (lane == 0) s_itx[cur ^ 1] = nxt;
+    }
+    __syncthreads();   // every slot read; the next item's descriptor in LDS
+
+    // the next item's queries and first copies go out before this item's
+    // output is written, so their latency overlaps the stores
+    const int itx_n = s_itx[cur ^ 1];
+    const Item<D> prev = it;
+    if (itx_n < n_items) {
+      it = item_of<D>(p, &s_desc[cur ^ 1], itx_n, per_entry, queue, wave, lane);
+      start_item(it, &s_desc[cur ^ 1]);
+    }
 
     // normalise and store: lane holds query qi, d = 32dt + 8i + 4(lane/32) + 0..3
     const float lt = halves_sum(l);
-    if (it.qi < it.n) {
+    if (prev.qi < prev.n) {
       const float inv = 1.f / lt;
-      uint16_t* orow = p.out + ((int64_t)(tok0 + it.qi) * p.hq + it.head) * D + 4 * (lane >> 5);
+      uint16_t* orow = p.out + ((int64_t)(prev.tok0 + prev.qi) * p.hq + prev.head) * D + 4 * (lane >> 5);
 #pragma unroll
       for (int dt = 0; dt < G::NDT; ++dt)
 #pragma unroll
@@ -550,7 +618,10 @@ prefill_kernel(PrefillParams p) {
               u32x2{pack_bf16(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv),
                     pack_bf16(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv)};
     }
+    cur ^= 1;
+    if (itx_n >= n_items) break;
   }
+  if (bad && lane == 0) atomicOr(&p.hdr->status, 2u);
 }
 
 }  // namespace
