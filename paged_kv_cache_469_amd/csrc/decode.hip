@@ -24,7 +24,10 @@
 // its registers.  V rows are loaded fully coalesced (16 lanes cover one
 // 256-byte row) with a permuted d order (tile t, row m <-> d = (D/16)*m + t)
 // and transposed to the A operand with v_perm in registers.  Next 32 keys'
-// K/V loads are issued before the current 32 keys are computed.
+// K/V loads are issued before the current 32 keys are computed.  The loads
+// are raw buffer loads ranged to the rows before the partition end (rows
+// past it and blocks outside the pool read as zeros, with no per-lane
+// branch), marked non-temporal.
 #include "kernels.hpp"
 
 namespace pkv {
@@ -37,41 +40,58 @@ struct KvRegs {
   uint32_t v[8][VW];
 };
 
+// Buffer views of one 16-key block of KV head g: K half and V half, each
+// ranged to the block's rows before the partition end (rows past it, and a
+// block outside the pool, read as zeros through the range check of the raw
+// buffer access, so the loads need no per-lane conditions).
+struct BlockRs {
+  __amdgpu_buffer_rsrc_t k, v;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;   // fourth descriptor word on gfx950
+// Cache policy of the K/V loads: non-temporal (each byte is read once per
+// step, so it should not displace what the caches hold for reuse).
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ BlockRs block_rs(const uint16_t* cache, int bid, bool ok, int nvalid,
+                                            int64_t block_bytes, int64_t row_bytes, int g,
+                                            int head_bytes) {
+  const char* base = reinterpret_cast<const char*>(cache) + (ok ? (int64_t)bid * block_bytes : 0) +
+                     (int64_t)g * head_bytes;
+  const int nrec = __builtin_amdgcn_readfirstlane(ok ? nvalid * (int)row_bytes : 0);
+  BlockRs r;
+  r.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kRsrcWord3);
+  r.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + kBlock * row_bytes), (short)0,
+                                          nrec, kRsrcWord3);
+  return r;
+}
+
+// K and V of 32 keys (two blocks): lane (m, j) loads K row m, d 8j + 32sl
+// .. +7 of each block, and V rows 4j .. 4j+3 of each block, d (D/16)m ..
+// (D/16)m + D/16 - 1.
 template <int D>
-__device__ __forceinline__ void load_kv(KvRegs<D>& r, const uint16_t* __restrict__ cache,
-                                        int64_t off0, int64_t off1, bool ok0, bool ok1,
-                                        int kb, int key1, int m, int j, int64_t row_elems) {
+__device__ __forceinline__ void load_kv(KvRegs<D>& r, const BlockRs& b0, const BlockRs& b1,
+                                        int m, int j, uint32_t row_bytes) {
   constexpr int NS = KvRegs<D>::NS;
   constexpr int VW = KvRegs<D>::VW;
   constexpr int NT = D / 16;
+  const uint32_t koff = m * row_bytes + 16 * j;
+  const uint32_t voff = 4 * j * row_bytes + 2 * NT * m;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int64_t off = b ? off1 : off0;
-    const bool okb = b ? ok1 : ok0;
-    const bool kval = okb && (kb + 16 * b + m < key1);
-    const uint16_t* kp = cache + off + m * row_elems + 8 * j;
+    const BlockRs& rs = b ? b1 : b0;
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      r.k[b][sl] = kval ? *reinterpret_cast<const u32x4*>(kp + 32 * sl) : z;
-    }
-  }
+    for (int sl = 0; sl < NS; ++sl)
+      r.k[b][sl] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, koff + 64 * sl, 0, kNonTemporal));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = i >> 2;
-    const int row = 4 * j + (i & 3);
-    const int64_t off = b ? off1 : off0;
-    const bool okb = b ? ok1 : ok0;
-    const bool vval = okb && (kb + 16 * b + row < key1);
-    const uint16_t* vp = cache + off + (int64_t)(kBlock + row) * row_elems + NT * m;
-    if constexpr (VW == 4) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      u32x4 x = vval ? *reinterpret_cast<const u32x4*>(vp) : z;
-      r.v[i][0] = x[0]; r.v[i][1] = x[1]; r.v[i][2] = x[2]; r.v[i][3] = x[3];
-    } else {
-      u32x2 z = {0u, 0u};
-      u32x2 x = vval ? *reinterpret_cast<const u32x2*>(vp) : z;
-      r.v[i][0] = x[0]; r.v[i][1] = x[1];
+    for (int rr = 0; rr < 4; ++rr) {
+      if constexpr (VW == 4) {
+        const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, voff, rr * row_bytes, kNonTemporal));
+        r.v[4 * b + rr][0] = x[0]; r.v[4 * b + rr][1] = x[1]; r.v[4 * b + rr][2] = x[2]; r.v[4 * b + rr][3] = x[3];
+      } else {
+        const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs.v, voff, rr * row_bytes, kNonTemporal));
+        r.v[4 * b + rr][0] = x[0]; r.v[4 * b + rr][1] = x[1];
+      }
     }
   }
 }
@@ -128,6 +148,7 @@ __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf
   }
 }
 
+// One wave per SIMD: forcing two (256 registers each) measured slower.
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_kernel(DecodeParams p) {
@@ -138,8 +159,8 @@ decode_kernel(DecodeParams p) {
   const int j = lane >> 4;
   const int n_items = p.hdr->n_decode * p.hkv;
   if (n_items == 0) return;   // no decode segment in this step: no queue traffic
-  const int64_t row_elems = (int64_t)p.hkv * D;
-  const int64_t block_elems = 2 * kBlock * row_elems;
+  const int64_t row_bytes = (int64_t)p.hkv * D * 2;
+  const int64_t block_bytes = 2 * kBlock * row_bytes;
 
   for (;;) {
     int it = 0;
@@ -181,34 +202,34 @@ decode_kernel(DecodeParams p) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    auto block_at = [&](int kb, int b, int64_t& off, bool& ok) {
-      const int blk = (kb - key0) / kBlock + b;
-      const bool exists = kb + kBlock * b < key1;
-      const int bid = exists ? __builtin_amdgcn_readlane(my_bid, blk) : -1;
-      ok = exists && bid >= 0 && (int64_t)bid < p.num_blocks;
-      off = ok ? (int64_t)bid * block_elems + (int64_t)g * D : 0;
+    // block b of the 32 keys starting at kb; its keys count as present
+    // (ok) when the block is inside the pool
+    auto block_at = [&](int kb, int b, bool& ok) -> BlockRs {
+      const int first = kb + kBlock * b;
+      const int nvalid = min(max(key1 - first, 0), kBlock);
+      const int bid = nvalid > 0 ? __builtin_amdgcn_readlane(my_bid, (first - key0) / kBlock) : -1;
+      ok = nvalid > 0 && bid >= 0 && (int64_t)bid < p.num_blocks;
+      return block_rs(p.cache, bid, ok, nvalid, block_bytes, row_bytes, g, D * 2);
     };
 
     KvRegs<D> ra, rb;
-    int64_t a0, a1, b0, b1;
     bool ao0, ao1, bo0, bo1;
-    block_at(key0, 0, a0, ao0);
-    block_at(key0, 1, a1, ao1);
-    load_kv<D>(ra, p.cache, a0, a1, ao0, ao1, key0, key1, m, j, row_elems);
+    {
+      const BlockRs x0 = block_at(key0, 0, ao0), x1 = block_at(key0, 1, ao1);
+      load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
+    }
     for (int kb = key0; kb < key1; kb += 64) {
       const int kn = kb + 32;
       if (kn < key1) {
-        block_at(kn, 0, b0, bo0);
-        block_at(kn, 1, b1, bo1);
-        load_kv<D>(rb, p.cache, b0, b1, bo0, bo1, kn, key1, m, j, row_elems);
+        const BlockRs x0 = block_at(kn, 0, bo0), x1 = block_at(kn, 1, bo1);
+        load_kv<D>(rb, x0, x1, m, j, (uint32_t)row_bytes);
       }
       attend_step<D>(ra, qf, o, m_run, l_run, kb, key1, ao0, ao1, j, p.scale_log2);
       if (kn >= key1) break;
       const int kn2 = kb + 64;
       if (kn2 < key1) {
-        block_at(kn2, 0, a0, ao0);
-        block_at(kn2, 1, a1, ao1);
-        load_kv<D>(ra, p.cache, a0, a1, ao0, ao1, kn2, key1, m, j, row_elems);
+        const BlockRs x0 = block_at(kn2, 0, ao0), x1 = block_at(kn2, 1, ao1);
+        load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
       }
       attend_step<D>(rb, qf, o, m_run, l_run, kn, key1, bo0, bo1, j, p.scale_log2);
     }
