@@ -23,6 +23,9 @@ generators, values N(0,1) drawn on the GPU with a seeded generator.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -206,6 +209,148 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+# HBM traffic of a kernel, from two rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
+# the plain 1 GiB copy of --copy-calibration.  The summary (a text file under
+# profiles/) records a hash of the kernel's sources; bench reports the
+# traffic only while the sources still hash the same.
+KERNEL_SOURCES = {
+    "decode_kernel": ["decode.hip", "common.hpp", "kernels.hpp"],
+    "prefill_kernel": ["prefill.hip", "common.hpp", "kernels.hpp"],
+}
+
+
+def _code_only(text):
+    """Source text without // comments and blank space, so that editing a
+    comment does not count as changing the kernel."""
+    out = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].strip()
+        if code:
+            out.append(" ".join(code.split()))
+    return "\n".join(out)
+
+
+def kernel_source_hash(kernel, read=None):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        path = os.path.join("paged_kv_cache_469_amd", "csrc", f)
+        if read is None:
+            with open(os.path.join(ROOT, path)) as fh:
+                text = fh.read()
+        else:
+            text = read(path)
+        h.update(_code_only(text).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    return float(fields["hbm_bytes_per_launch"])
+
+
+def _counter_means(path_glob, name_filter):
+    vals = {}
+    for f in glob.glob(path_glob):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if name_filter(r["Kernel_Name"]):
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def pmc_summary(args):
+    """Turns the four counter runs into the summary text bench reads back."""
+    copy_kib = (1 << 30) / 1024.0
+    cf, _ = _counter_means(os.path.join(args.calib_fetch, "*counter_collection.csv"), lambda n: "copyBuffer" in n)
+    cw, _ = _counter_means(os.path.join(args.calib_write, "*counter_collection.csv"), lambda n: "copyBuffer" in n)
+    kf, nf = _counter_means(os.path.join(args.fetch, "*counter_collection.csv"), lambda n: args.kernel in n)
+    kw, nw = _counter_means(os.path.join(args.write, "*counter_collection.csv"), lambda n: args.kernel in n)
+    f_scale = copy_kib / cf["FETCH_SIZE"]
+    w_scale = copy_kib / cw["WRITE_SIZE"]
+    fetch = kf["FETCH_SIZE"] * f_scale * 1024.0
+    write = kw["WRITE_SIZE"] * w_scale * 1024.0
+    lines = [
+        f"# HBM traffic of {args.kernel}<128>, workload {args.workload}",
+        "#",
+        "# Commands (from the repository root, on one MI355X):",
+        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {args.kernel} -f csv -d <F> -o k -- "
+        f"python bench.py --workload {args.workload} --steps 3 --warmup 1 --no-prefill --no-cpu-baseline",
+        f"#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {args.kernel} -f csv -d <W> -o k -- "
+        f"python bench.py --workload {args.workload} --steps 3 --warmup 1 --no-prefill --no-cpu-baseline",
+        "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <CF> -o copy -- python bench.py --copy-calibration",
+        "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <CW> -o copy -- python bench.py --copy-calibration",
+        f"#   python bench.py --pmc-summary --kernel {args.kernel} --workload {args.workload} "
+        "--fetch <F> --write <W> --calib-fetch <CF> --calib-write <CW>",
+        "#",
+        "# The copy moves 1 GiB each way; the counters' KiB for it give the scales.",
+        f"copy_fetch_kib_per_dispatch: {cf['FETCH_SIZE']:.1f}",
+        f"copy_write_kib_per_dispatch: {cw['WRITE_SIZE']:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"kernel_dispatches: fetch {nf.get('FETCH_SIZE', 0)} write {nw.get('WRITE_SIZE', 0)}",
+        f"kernel_fetch_kib_per_dispatch: {kf['FETCH_SIZE']:.1f}",
+        f"kernel_write_kib_per_dispatch: {kw['WRITE_SIZE']:.1f}",
+        f"hbm_fetch_bytes_per_launch: {fetch:.0f}",
+        f"hbm_write_bytes_per_launch: {write:.0f}",
+        f"hbm_bytes_per_launch: {fetch + write:.0f}",
+        f"source_sha256_16: {kernel_source_hash(args.kernel)}",
+    ]
+    print("\n".join(lines))
+
+
+def trace_summary(args):
+    """Per-kernel durations from a rocprofv3 --kernel-trace CSV of the default
+    bench command, split into its two phases (decode_8b, then prefill_8b) by
+    counting the KV-write dispatches that open every step."""
+    path = glob.glob(os.path.join(args.trace, "*kernel_trace.csv"))[0]
+    with open(path) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+    rows = [r for r in rows if "pkv::" in r["Kernel_Name"]]
+    n_dec = args.warmup + args.steps                     # decode_8b steps
+    phases, seen = {"decode_8b": [], "prefill_8b": []}, 0
+    for r in rows:
+        if "kv_write" in r["Kernel_Name"]:
+            seen += 1
+        phases["decode_8b" if seen <= n_dec else "prefill_8b"].append(r)
+    out = [f"# Kernel trace: default bench (decode_8b headline, prefill_8b line item)", "",
+           "Command (from the repository root, on one MI355X):", "",
+           f"    rocprofv3 --kernel-trace --stats -f csv -d <T> -o kt -- python bench.py "
+           f"--steps {args.steps} --warmup {args.warmup} --no-cpu-baseline",
+           f"    python bench.py --trace-summary --trace <T> --steps {args.steps} --warmup {args.warmup}",
+           "", "Durations in microseconds (end - start of each dispatch).", ""]
+    for ph, rs in phases.items():
+        by = {}
+        for r in rs:
+            name = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            by.setdefault(name, {"d": [], "r": r})["d"].append(d)
+        out += [f"### phase: {ph}", "", "| kernel | calls | avg us | min us | max us | grid (threads) | wg | vgpr | lds B |",
+                "|---|---|---|---|---|---|---|---|---|"]
+        for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1]["d"])):
+            d, r = v["d"], v["r"]
+            out.append(f"| {name} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} | "
+                       f"{r['Grid_Size_X']} | {r['Workgroup_Size_X']} | {r['VGPR_Count']} | {r['LDS_Block_Size']} |")
+        out.append("")
+    print("\n".join(out))
+
+
 def make_workload(name):
     import torch
     import workloads
@@ -243,10 +388,26 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=160, help="decode requests the oracle runs")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--pmc-summary", action="store_true",
+                    help="summarise four rocprofv3 counter runs (see --fetch .. --calib-write)")
+    ap.add_argument("--trace-summary", action="store_true",
+                    help="summarise a rocprofv3 kernel-trace CSV of the default bench (--trace DIR)")
+    ap.add_argument("--trace")
+    ap.add_argument("--kernel", default="decode_kernel")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--calib-fetch")
+    ap.add_argument("--calib-write")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), the reference kernel "
                          "that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -294,7 +455,8 @@ def main():
         ach = pre_flops / (us["prefill"] * 1e-6) / 1e12
         out["roofline"] = {"kernel": "prefill_kernel<128>", "bound": "mfma", "achieved": ach,
                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                           "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                           "traffic": stored_traffic("prefill_kernel", args.workload)}
     elif args.workload == "tiny_mixed":
         out.update(value=kv_bytes / (ms * 1e-3) / 1e9, unit="GB/s")
         out["roofline"] = None
@@ -303,7 +465,8 @@ def main():
         ach = dec_bytes / (us["decode"] * 1e-6) / 1e9
         out["roofline"] = {"kernel": "decode_kernel<128>", "bound": "hbm", "achieved": ach,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "traffic": None}
+                           "traffic": stored_traffic("decode_kernel", args.workload),
+                           "algorithmic_bytes": dec_bytes}
     out["config"] = cfg
     out["kernels_us"] = us
     if args.workload == "long_decode_70b":
@@ -323,7 +486,7 @@ def main():
                           "roofline": {"kernel": "prefill_kernel<128>", "bound": "mfma",
                                        "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
                                        "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                                       "traffic": None},
+                                       "traffic": stored_traffic("prefill_kernel", "prefill_8b")},
                           "kernels_us": pr["us"]}
 
     if not args.no_cpu_baseline:

@@ -9,12 +9,11 @@
 // the bf16 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
 // Work item: (segment, query tile of QT queries, KV head, head chunk), run by
-// one workgroup of 8 waves, two per SIMD.  Each wave owns one query head and
-// 32 queries; the waves share the KV head, so each 64-key K/V tile is copied
-// from its four 16-token blocks once into LDS and read by all eight.  The
-// copy is staged through registers: wave w of group A loads K of block w of
-// the tile, wave w of group B loads V of it, and each writes its block into
-// swizzled LDS rows a step later.
+// one workgroup of 8 waves, two per SIMD, in a persistent grid fed by one
+// queue per XCD.  Each wave owns one query head and 32 queries; the waves
+// share the KV head, so each 64-key K/V tile is copied from its four
+// 16-token blocks once into LDS (straight from global memory, one block per
+// wave of group A for each of K and V) and read by all eight.
 //
 // Per wave and tile:
 //   S^T[key, q] = K[key, :] . Q[q, :]         Q held in registers (B operand)
@@ -25,18 +24,18 @@
 // The C layout of S^T (lane = query) is the B operand layout of the second
 // product, so P never leaves registers.  The running maximum m is lazy: it
 // moves only when a tile's maximum exceeds it by more than 8 (log2 units),
-// so rescaling O is rare and P stays below 2^8; the normaliser l sums the
-// bf16-rounded P that the numerator uses.
+// so rescaling O is rare and P stays below 2^8; the normaliser l sums P in
+// fp32, the numerator uses P rounded to bf16 (the MFMA operand).
 //
 // Ping-pong: waves 0-3 (group A) and 4-7 (group B) sit on the four SIMDs in
 // pairs and alternate phases, separated by workgroup barriers.  While group
-// A issues the matrix products of tile t (QK^T of t, PV of t-1), group B runs
-// the softmax of tile t-1 on the vector ALUs of the same SIMDs, and then the
-// other way round; so the matrix cores and the vector ALUs work at the same
-// time.  Loads run two tiles ahead and LDS writes one tile ahead, so each
-// of K and V has two LDS slots.  K/V rows at or past L, and rows of blocks outside the
-// pool, come from a zero line, so poison in unused pool memory never reaches
-// the products.
+// A issues the matrix products (QK^T of tile t, PV of tile t-1), group B runs
+// its softmax on the vector ALUs of the same SIMDs, and then the other way
+// round; so the matrix cores and the vector ALUs work at the same time.  K
+// and V have three LDS slots each; copies run two tiles (K) and one tile (V)
+// ahead.  K/V rows past the item's last needed key, and rows of blocks
+// outside the pool, arrive as zeros, so poison in unused pool memory never
+// reaches the products.
 #include "kernels.hpp"
 
 namespace pkv {
