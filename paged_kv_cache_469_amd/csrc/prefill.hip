@@ -392,13 +392,15 @@ struct Slots {
 // barrier 2t opening group A's step t:
 //   group A: matrix phase (2t, 2t+1], softmax phase (2t+1, 2t+2];
 //   group B: matrix phase (2t+1, 2t+2], softmax phase (2t+2, 2t+3].
-// Copies: when its softmax phase of step t starts, wave w of group A copies
-// block w of K(t+2) into the slot of K(t-1) and block w of V(t+1) into the
-// slot of V(t-2), and waits for them before its closing barrier of step t+1.
+// Copies, each when the wave's softmax phase of step t starts:
+//   wave w of group A copies block w of K(t+2) into the slot of K(t-1) and
+//     waits for it before its closing barrier of step t+1 (barrier 2t+4);
+//   wave w of group B copies block w of V(t+1) into the slot of V(t-2) and
+//     waits for it before the end of its matrix phase of step t+1 (2t+4).
 // The slots' last readers (group B's products of step t-1) finished by
 // barrier 2t; the first readers of the new tiles (group A's QK(t+2) and
 // PV(t+1)) start after barrier 2t+4.  The products of both groups between
-// those barriers read the other slots.  Group B copies nothing.
+// those barriers read the other slots.
 template <int D, int R>
 __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>& it, const Slots<D>& sl,
                                           int t, bool group_b, int wave, int lane,
@@ -419,16 +421,18 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   // finite values, so the extra products change nothing.
   qk<D>(sc, q, ak, sl.k[R]);
   pv<D>(o, pr, av, sl.v[RP]);
+  if (group_b) copies_landed<0>();   // V(t), copied during the step before
   wg_barrier();
   if (!group_b) {
-    const int bk = 4 * (t + 2) + wq, bv = 4 * (t + 1) + wq;   // blocks of K(t+2) and V(t+1)
+    const int bk = 4 * (t + 2) + wq;   // block of K(t+2)
     const int bid_k = __builtin_amdgcn_readfirstlane(bt[(bk / kWindow) & 1][bk % kWindow]);
-    const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
     copy_block<D>(p, bid_k, kKeys * (t + 2) + kBlock * wq, it.kmax, it.g, false, ck,
                   lds_addr(sl.k[RP]) + wq * kBlockBytes, bad);
+  } else {
+    const int bv = 4 * (t + 1) + wq;   // block of V(t+1)
+    const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
     copy_block<D>(p, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
                   lds_addr(sl.v[RN]) + wq * kBlockBytes, bad);
-  } else {
     const int w = t / 64 + 1;   // the window after the current one
     if ((t & 63) == 1 && kWindow * w < it.nblk) {
       bt_next = window_entry(it.bt_row, w, wave - kWaves / 2, lane, it.nblk);
@@ -457,8 +461,8 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
 #pragma unroll
       for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
   }
-  // group A: the copies of the step before have landed (this step's may not)
-  if (!group_b) copies_landed<2 * CopyOff<D>::NCH>();
+  // group A: the copy of the step before has landed (this step's may not)
+  if (!group_b) copies_landed<CopyOff<D>::NCH>();
   __syncthreads();
 }
 
@@ -585,10 +589,8 @@ prefill_kernel(PrefillParams p) {
       if (t + 2 <= it.ntiles)
         tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
     }
-    if (!group_b) {
-      copies_landed<0>();   // nothing in flight into the slots past the item
-      wg_barrier();         // group B's last step ends here
-    }
+    copies_landed<0>();     // nothing in flight into the slots past the item
+    if (!group_b) wg_barrier();   // group B's last step ends here
     if (wave == kWaves / 2) {
       if (lane < 16) reinterpret_cast<int32_t*>(&s_desc[cur ^ 1])[lane] = nxt_word;
       if (lane == 0) s_itx[cur ^ 1] = nxt;
