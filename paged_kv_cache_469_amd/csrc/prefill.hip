@@ -376,13 +376,13 @@ __device__ __forceinline__ Item<D> item_of(const PrefillParams& p, const Prefill
   return it;
 }
 
-// LDS slots: K and V of three tiles (tile j in slot j % 3), as separate
-// objects so the compiler can tell that a copy into one slot never touches
-// the slot being read.
+// LDS slots: K of three tiles (tile j in slot j % 3) and V of two (slot
+// j % 2), as separate objects so the compiler can tell that a copy into one
+// slot never touches the slot being read.
 template <int D>
 struct Slots {
   PKV_LDS char* k[3];
-  PKV_LDS char* v[3];
+  PKV_LDS char* v[2];
 };
 
 // One tile step t (R = t % 3) of one wave: QK(t) and PV(t-1) on the
@@ -395,10 +395,11 @@ struct Slots {
 // Copies, each when the wave's softmax phase of step t starts:
 //   wave w of group A copies block w of K(t+2) into the slot of K(t-1) and
 //     waits for it before its closing barrier of step t+1 (barrier 2t+4);
-//   wave w of group B copies block w of V(t+1) into the slot of V(t-2) and
+//   wave w of group B copies block w of V(t+1) into the slot of V(t-1) and
 //     waits for it before the end of its matrix phase of step t+1 (2t+4).
-// The slots' last readers (group B's products of step t-1) finished by
-// barrier 2t; the first readers of the new tiles (group A's QK(t+2) and
+// The K slot's last readers (group B's QK(t-1)) finished by barrier 2t; the
+// V slot's (group B's PV(t-1)) by barrier 2t+2, which the copying wave has
+// passed.  The first readers of the new tiles (group A's QK(t+2) and
 // PV(t+1)) start after barrier 2t+4.  The products of both groups between
 // those barriers read the other slots.
 template <int D, int R>
@@ -411,16 +412,17 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
                                           const CopyOff<D>& cv, int32_t (*bt)[kWindow],
                                           int& bt_next, uint32_t& bad, int& nxt, int& nxt_word,
                                           int n_items, int per_entry) {
-  constexpr int RP = (R + 2) % 3;   // slot of tiles t - 1 and t + 2
-  constexpr int RN = (R + 1) % 3;   // slot of tiles t + 1 and t - 2
+  constexpr int RK = R;             // K slot of tile t
+  constexpr int RP = (R + 2) % 3;   // K slot of tiles t - 1 and t + 2
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
   const int wq = wave & 3;
   // Matrix phase: QK(t) and PV(t-1) run on every step, as one scheduling
   // region.  A tile the wave does not use (before the first, past the last,
   // or past every key its queries see) has P = 0, and every slot read holds
   // finite values, so the extra products change nothing.
-  qk<D>(sc, q, ak, sl.k[R]);
-  pv<D>(o, pr, av, sl.v[RP]);
+  PKV_LDS char* const v_prev = (t & 1) ? sl.v[0] : sl.v[1];   // V slot of tiles t - 1 and t + 1
+  qk<D>(sc, q, ak, sl.k[RK]);
+  pv<D>(o, pr, av, v_prev);
   if (group_b) copies_landed<0>();   // V(t), copied during the step before
   wg_barrier();
   if (!group_b) {
@@ -432,7 +434,7 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
     const int bv = 4 * (t + 1) + wq;   // block of V(t+1)
     const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
     copy_block<D>(p, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
-                  lds_addr(sl.v[RN]) + wq * kBlockBytes, bad);
+                  lds_addr(v_prev) + wq * kBlockBytes, bad);
     const int w = t / 64 + 1;   // the window after the current one
     if ((t & 63) == 1 && kWindow * w < it.nblk) {
       bt_next = window_entry(it.bt_row, w, wave - kWaves / 2, lane, it.nblk);
@@ -466,6 +468,107 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   __syncthreads();
 }
 
+// Queries of one wave (32 rows from row qw of the segment, one head) into
+// its LDS area with global -> LDS copies: copy k puts rows RPI*k .. of the
+// area in place, lane i the 16-byte chunk at position i % CPR of row
+// RPI*k + i / CPR, which holds chunk position ^ (row % CPR) of that row (the
+// same swizzle as K), so the 16 lanes of a row read one contiguous row.  Rows
+// past the segment's end arrive as zeros (range-checked buffer).
+template <int D>
+__device__ __forceinline__ void copy_queries(const PrefillParams& p, int tok0, int qw, int n, int head,
+                                             int lane, uint32_t lds_dst) {
+  using G = Geo<D>;
+  // the per-lane offsets are recomputed here (a few instructions per item)
+  // rather than hoisted out of the item loop, where they would hold
+  // registers through every tile step
+  asm volatile("" : "+v"(lane));
+  constexpr int RPI = 1024 / G::ROWB;          // rows per copy
+  constexpr int NQ = 32 / RPI;                 // copies per wave
+  const int64_t rstride = p.q_stride * 2;      // bytes between query rows
+  const int rows = min(max(n - qw, 0), 32);
+  const char* base = reinterpret_cast<const char*>(p.q) + ((int64_t)(tok0 + qw) * p.q_stride + (int64_t)head * D) * 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(base), (short)0,
+      __builtin_amdgcn_readfirstlane(rows > 0 ? (int)(rows * rstride) : 0), kRsrcWord3);
+  uint32_t off[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int r = RPI * k + lane / G::CPR;
+    off[k] = (uint32_t)(r * rstride) + 16 * k_chunk<D>(r, lane % G::CPR);
+  }
+  if constexpr (NQ == 8) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %9, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %9, 0 offen lds"
+        :: "s"(lds_dst), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]),
+           "v"(off[5]), "v"(off[6]), "v"(off[7]), "s"(rs)
+        : "memory", "scc");
+  } else {
+    static_assert(NQ == 4, "copies per wave");
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
+        :: "s"(lds_dst), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rs)
+        : "memory", "scc");
+  }
+}
+
+// The wave's queries from its LDS area into the B operands of QK^T (lane:
+// row lane % 32, d-chunk 2i + lane / 32 of slab i), sign applied.
+template <int D>
+__device__ __forceinline__ void read_queries(u32x4 (&q)[Geo<D>::NSL], const PKV_LDS char* io,
+                                             int lane, uint32_t q_sign) {
+  using G = Geo<D>;
+  const int r = lane & 31;
+#pragma unroll
+  for (int i = 0; i < G::NSL; ++i)
+    q[i] = *reinterpret_cast<const PKV_LDS u32x4*>(io + r * G::ROWB + 16 * k_chunk<D>(r, 2 * i + (lane >> 5))) ^ q_sign;
+}
+
+// Normalise the wave's output and store it: bf16 pairs into its LDS area
+// (lane: row lane % 32, d = 32dt + 8i + 4(lane/32) + 0..3, same swizzle),
+// then whole rows out, 16 lanes per 256-byte row, through a range-checked
+// buffer that drops rows past the segment's end.
+template <int D>
+__device__ __forceinline__ void store_output(const PrefillParams& p, const f32x16 (&o)[Geo<D>::NDT],
+                                             float lt, int tok0, int qw, int n, int head, int lane,
+                                             PKV_LDS char* io) {
+  using G = Geo<D>;
+  constexpr int RPI = 1024 / G::ROWB;
+  constexpr int NQ = 32 / RPI;
+  asm volatile("" : "+v"(lane));   // offsets computed here, not hoisted (see copy_queries)
+  const float inv = __builtin_amdgcn_rcpf(lt);
+  const int r = lane & 31;
+#pragma unroll
+  for (int dt = 0; dt < G::NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<PKV_LDS u32x2*>(io + r * G::ROWB + 16 * k_chunk<D>(r, 4 * dt + i) + 8 * (lane >> 5)) =
+          u32x2{pack_bf16(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv),
+                pack_bf16(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv)};
+  const int64_t rstride = (int64_t)p.hq * D * 2;   // bytes between output rows
+  const int rows = min(max(n - qw, 0), 32);
+  const char* base = reinterpret_cast<const char*>(p.out) + ((int64_t)(tok0 + qw) * p.hq + head) * D * 2;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(base), (short)0,
+      __builtin_amdgcn_readfirstlane(rows > 0 ? (int)(rows * rstride) : 0), kRsrcWord3);
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int rr = RPI * k + lane / G::CPR;
+    const int pc = lane % G::CPR;
+    const u32x4 v = *reinterpret_cast<const PKV_LDS u32x4*>(io + rr * G::ROWB + 16 * pc);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (uint32_t)(rr * rstride) + 16 * k_chunk<D>(rr, pc), 0, 0);
+  }
+}
+
 template <int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
@@ -475,17 +578,18 @@ prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char k2_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char v0_lds[G::TILEB];
   __shared__ __attribute__((aligned(1024))) char v1_lds[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v2_lds[G::TILEB];
+  // per wave: its queries on their way in, its output on its way out
+  __shared__ __attribute__((aligned(1024))) char io_lds[kWaves][32 * G::ROWB];
   __shared__ PrefillItem s_desc[2];   // the current and the next item
   __shared__ int s_itx[2];
   __shared__ int32_t s_bt[2][kWindow];   // block-table windows of the current item
   const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds, (PKV_LDS char*)k2_lds},
-                       {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds, (PKV_LDS char*)v2_lds}};
+                       {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds}};
+  PKV_LDS char* const io = (PKV_LDS char*)io_lds[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool group_b = wave >= kWaves / 2;
-  const int hw = p.heads_per_item;
   const int per_entry = (p.hkv / p.num_queues) * p.head_chunks;
   const int queue = blockIdx.x % p.num_queues;
   const int n_items = p.hdr->n_prefill * per_entry;
@@ -530,22 +634,15 @@ prefill_kernel(PrefillParams p) {
   u32x4 q[G::NSL];
   int bt_next = 0;   // group B: a lane's entry of the next block-table window
   uint32_t bad = 0;
-  // Start of an item: its queries into registers, the V slot of tile -1
-  // cleared (the first step multiplies a zero P by it, so it must hold
-  // finite values), the copies of K(0), K(1) (group A) and V(0) (group B),
+  // Start of an item: its queries into the wave's LDS area, the V slot of
+  // tile -1 cleared (the first step multiplies a zero P by it, so it must
+  // hold finite values), the copies of K(0), K(1) (group A) and V(0) (group B),
   // one block per wave each, with the block ids from the descriptor, and
   // (group B) the loads of block-table window 0, written when the item runs.
   auto start_item = [&](const Item<D>& nx, const PrefillItem* d) {
-    const uint16_t* qrow =
-        p.q + (int64_t)(nx.tok0 + nx.qi) * p.q_stride + (int64_t)nx.head * D + 8 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < G::NSL; ++i) {   // sign applied once they have arrived
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (nx.qi < nx.n) v = *reinterpret_cast<const u32x4*>(qrow + 16 * i);
-      q[i] = v;
-    }
+    copy_queries<D>(p, nx.tok0, nx.qw, nx.n, nx.head, lane, lds_addr(io));
     for (int i = threadIdx.x; i < G::TILEB / 16; i += kWaves * 64)
-      reinterpret_cast<PKV_LDS u32x4*>(sl.v[2])[i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<PKV_LDS u32x4*>(sl.v[1])[i] = u32x4{0u, 0u, 0u, 0u};
     const int bid0 = __builtin_amdgcn_readfirstlane(d->bid[wq]);
     const int bid1 = __builtin_amdgcn_readfirstlane(d->bid[4 + wq]);   // block of tile 1
     if (group_b) bt_next = window_entry(nx.bt_row, 0, wave - kWaves / 2, lane, nx.nblk);
@@ -575,19 +672,18 @@ prefill_kernel(PrefillParams p) {
       for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
 
     if (group_b) s_bt[0][64 * (wave - kWaves / 2) + lane] = bt_next;   // window 0
-    copies_landed<0>();   // the copies and the query loads
+    copies_landed<0>();   // the copies of K/V and of the queries
     __syncthreads();   // K(0), K(1), V(0), window 0 in LDS, the V slot of tile -1 cleared
-#pragma unroll
-    for (int i = 0; i < G::NSL; ++i) q[i] ^= p.q_sign;
+    read_queries<D>(q, io, lane, p.q_sign);
     // asked for only now, so the wait for the copies above does not include it
     if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[queue], 1);
     if (group_b) wg_barrier();
     for (int t = 0; t <= it.ntiles; t += 3) {
       tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
-      if (t + 1 <= it.ntiles)
-        tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
-      if (t + 2 <= it.ntiles)
-        tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
+      if (t + 1 > it.ntiles) break;
+      tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
+      if (t + 2 > it.ntiles) break;
+      tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
     }
     copies_landed<0>();     // nothing in flight into the slots past the item
     if (!group_b) wg_barrier();   // group B's last step ends here
@@ -597,28 +693,15 @@ prefill_kernel(PrefillParams p) {
     }
     __syncthreads();   // every slot read; the next item's descriptor in LDS
 
-    // the next item's queries and first copies go out before this item's
-    // output is written, so their latency overlaps the stores
     const int itx_n = s_itx[cur ^ 1];
     const Item<D> prev = it;
-    if (itx_n < n_items) {
-      it = item_of<D>(p, &s_desc[cur ^ 1], itx_n, per_entry, queue, wave, lane);
-      start_item(it, &s_desc[cur ^ 1]);
-    }
+    if (itx_n < n_items) it = item_of<D>(p, &s_desc[cur ^ 1], itx_n, per_entry, queue, wave, lane);
 
-    // normalise and store: lane holds query qi, d = 32dt + 8i + 4(lane/32) + 0..3
-    const float lt = halves_sum(l);
-    if (prev.qi < prev.n) {
-      const float inv = 1.f / lt;
-      uint16_t* orow = p.out + ((int64_t)(prev.tok0 + prev.qi) * p.hq + prev.head) * D + 4 * (lane >> 5);
-#pragma unroll
-      for (int dt = 0; dt < G::NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * i) =
-              u32x2{pack_bf16(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv),
-                    pack_bf16(o[dt][4 * i + 2] * inv, o[dt][4 * i + 3] * inv)};
-    }
+    // normalise; out through the wave's LDS area, so the stores are whole rows
+    store_output<D>(p, o, halves_sum(l), prev.tok0, prev.qw, prev.n, prev.head, lane, io);
+    // the next item's queries (into the same area, once this wave's reads of
+    // it have returned: the stores above consumed them) and first copies
+    if (itx_n < n_items) start_item(it, &s_desc[cur ^ 1]);
     cur ^= 1;
     if (itx_n >= n_items) break;
   }
