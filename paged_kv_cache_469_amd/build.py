@@ -30,8 +30,11 @@ FLAGS = [
 # operand reads several MFMAs ahead instead of one at a time.  Its scores are
 # never NaN (unused rows come from a zero line), so fmaxf needs no NaN
 # quieting of its operands (-fno-honor-nans; infinities are still honoured).
+# Its one-lane atomics stay plain atomics: the atomic optimizer would wait
+# for the returned value right after the atomic, which stalls the wave.
 PER_FILE = {
-    "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp", "-fno-honor-nans"],
+    "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp", "-fno-honor-nans",
+                    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 
 

@@ -392,14 +392,16 @@ struct Slots {
 // barrier 2t opening group A's step t:
 //   group A: matrix phase (2t, 2t+1], softmax phase (2t+1, 2t+2];
 //   group B: matrix phase (2t+1, 2t+2], softmax phase (2t+2, 2t+3].
-// Copies, each when the wave's softmax phase of step t starts:
-//   wave w of group A copies block w of K(t+2) into the slot of K(t-1) and
-//     waits for it before its closing barrier of step t+1 (barrier 2t+4);
-//   wave w of group B copies block w of V(t+1) into the slot of V(t-1) and
-//     waits for it before the end of its matrix phase of step t+1 (2t+4).
+// Copies:
+//   wave w of group A copies block w of K(t+2) into the slot of K(t-1) at
+//     the end of its matrix phase of step t, and waits for it before its
+//     closing barrier of step t+1 (barrier 2t+4);
+//   wave w of group B copies block w of V(t+1) into the slot of V(t-1) when
+//     its softmax phase of step t starts, and waits for it before the end of
+//     its matrix phase of step t+1 (2t+4).
 // The K slot's last readers (group B's QK(t-1)) finished by barrier 2t; the
-// V slot's (group B's PV(t-1)) by barrier 2t+2, which the copying wave has
-// passed.  The first readers of the new tiles (group A's QK(t+2) and
+// V slot's (group B's PV(t-1)) by barrier 2t+2; the copying wave has passed
+// both.  The first readers of the new tiles (group A's QK(t+2) and
 // PV(t+1)) start after barrier 2t+4.  The products of both groups between
 // those barriers read the other slots.
 template <int D, int R>
@@ -423,24 +425,22 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   PKV_LDS char* const v_prev = (t & 1) ? sl.v[0] : sl.v[1];   // V slot of tiles t - 1 and t + 1
   qk<D>(sc, q, ak, sl.k[RK]);
   pv<D>(o, pr, av, v_prev);
-  if (group_b) copies_landed<0>();   // V(t), copied during the step before
-  wg_barrier();
   if (!group_b) {
+    // after the products are issued, while the last of them run
     const int bk = 4 * (t + 2) + wq;   // block of K(t+2)
     const int bid_k = __builtin_amdgcn_readfirstlane(bt[(bk / kWindow) & 1][bk % kWindow]);
     copy_block<D>(p, bid_k, kKeys * (t + 2) + kBlock * wq, it.kmax, it.g, false, ck,
                   lds_addr(sl.k[RP]) + wq * kBlockBytes, bad);
-  } else {
-    const int bv = 4 * (t + 1) + wq;   // block of V(t+1)
-    const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
-    copy_block<D>(p, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
-                  lds_addr(v_prev) + wq * kBlockBytes, bad);
+  }
+  if (group_b) copies_landed<0>();   // V(t), copied during the step before
+  wg_barrier();
+  if (group_b) {
+    // Uses of values loaded during earlier steps come before this step's
+    // copy: the compiler waits for those loads there (every load of the
+    // wave has landed by then, before its matrix phase ended), so nothing
+    // waits for the copy.
     const int w = t / 64 + 1;   // the window after the current one
-    if ((t & 63) == 1 && kWindow * w < it.nblk) {
-      bt_next = window_entry(it.bt_row, w, wave - kWaves / 2, lane, it.nblk);
-    } else if ((t & 63) == 2 && kWindow * w < it.nblk) {
-      bt[w & 1][64 * (wave - kWaves / 2) + lane] = bt_next;
-    }
+    if ((t & 63) == 2 && kWindow * w < it.nblk) bt[w & 1][64 * (wave - kWaves / 2) + lane] = bt_next;
     if (wave == kWaves / 2 && t == 1) {
       // the next item: its index (asked for when this item started) and its
       // descriptor, one dword per lane, written to LDS when this item ends
@@ -448,6 +448,11 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
       const int32_t* src = reinterpret_cast<const int32_t*>(p.items + min(nxt, n_items - 1) / per_entry);
       nxt_word = src[lane & 15];
     }
+    const int bv = 4 * (t + 1) + wq;   // block of V(t+1)
+    const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
+    copy_block<D>(p, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
+                  lds_addr(v_prev) + wq * kBlockBytes, bad);
+    if ((t & 63) == 1 && kWindow * w < it.nblk) bt_next = window_entry(it.bt_row, w, wave - kWaves / 2, lane, it.nblk);
   }
   // tile t for the softmax; tiles no query of the wave sees are skipped
   const bool do_t = it.active && t < it.ntiles && kKeys * t < it.kend;
