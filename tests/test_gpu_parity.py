@@ -68,6 +68,10 @@ EDGE = [
     ("g16_d128", dict(hq=32, hkv=2, d=128, segs=[(1, 513), (70, 100)])),
     ("zero_len_segments", dict(hq=32, hkv=8, d=128, segs=[(0, 0), (1, 33), (0, 40), (7, 7)])),
     ("block_multiples", dict(hq=32, hkv=8, d=128, segs=[(1, 16), (1, 32), (1, 1024), (16, 16), (64, 128)])),
+    # a few new tokens at the end of a long history (a speculative-decoding
+    # verify step): n = 2..8, beside single-token decodes
+    ("short_chunks", dict(hq=32, hkv=8, d=128, segs=[(2, 3001), (4, 5003), (1, 4000), (5, 1237),
+                                                     (8, 8200), (3, 67)])),
 ]
 
 
