@@ -51,6 +51,8 @@ DESCRIPTIONS = {
                   "(64 share a 1024-token prefix) + one 2048-token chunk over 16384 cached tokens",
     "long_decode_70b": "70B-shaped layer share: 64 requests x 1 new token over U[32768,131072]; "
                        "64 q / 8 kv heads, head_dim 128; pool ~0.92 of free HBM",
+    "spec_verify_8b": "8B-shaped speculative-decoding check: 128 requests x 4 new tokens (3 drafted) "
+                      "over cached context U[2048,16384]; 32 q / 8 kv heads, head_dim 128",
 }
 
 
@@ -435,8 +437,10 @@ def main():
     us = main_res["us"]
     kv_bytes = wl.kv_bytes_unique()
     flops = wl.attention_flops()
-    decode_segs = np.nonzero(wl.new_tokens == 1)[0]
-    prefill_segs = np.nonzero(wl.new_tokens > 1)[0]
+    # segments on the split-context decode path: n * G <= 16 and n <= 8
+    max_dec = min(8, 16 // (wl.num_q_heads // wl.num_kv_heads))
+    decode_segs = np.nonzero((wl.new_tokens >= 1) & (wl.new_tokens <= max_dec))[0]
+    prefill_segs = np.nonzero(wl.new_tokens > max_dec)[0]
     dec_bytes = int(wl.seq_lens[decode_segs].astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
     if wl.shared_prefix:
         dec_bytes = kv_bytes - int(wl.seq_lens[prefill_segs].astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
@@ -490,7 +494,7 @@ def main():
                           "kernels_us": pr["us"]}
 
     if not args.no_cpu_baseline:
-        if args.workload in ("decode_8b", "long_decode_70b", "cb_step_8b"):
+        if args.workload in ("decode_8b", "long_decode_70b", "cb_step_8b", "spec_verify_8b"):
             import workloads
             base_wl = workloads.make("decode_8b") if args.workload == "decode_8b" else wl
             if args.workload == "decode_8b":

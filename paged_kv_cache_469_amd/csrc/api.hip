@@ -47,6 +47,11 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kQueryTileMin = 32;   // smallest prefill query tile (heads_per_item = 4)
 
+// Segments with at most this many new tokens take the split-context decode
+// path: their n * G query rows must fit the 16 columns of its products, and
+// n stays within the few tokens of a speculative-decoding check.
+int32_t max_decode_tokens(int32_t group) { return std::min(8, 16 / std::max(1, group)); }
+
 // Tokens per decode partition.  Automatic choice: the largest of 1024 .. 64
 // that still gives at least 8192 wave-sized items for the longest allowed
 // context (the items then outnumber the chip's resident waves several times,
@@ -68,7 +73,8 @@ struct Layout {
   int32_t pmax = 0;
   int64_t decode_cap = 0;
   int64_t prefill_cap = 0;
-  size_t decode_items = 0, prefill_items = 0, part_ml = 0, part_o = 0, total = 0;
+  int64_t rows_cap = 0;   // partial rows: one per new token of a decode segment
+  size_t decode_items = 0, prefill_items = 0, seg_row = 0, part_ml = 0, part_o = 0, total = 0;
 };
 
 Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -79,15 +85,20 @@ Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int
   l.pmax = (int32_t)std::max<int64_t>(1, (max_len + l.part_tokens - 1) / l.part_tokens);
   l.decode_cap = (int64_t)num_seqs * l.pmax;
   l.prefill_cap = (num_tokens + kQueryTileMin - 1) / kQueryTileMin + (int64_t)num_seqs;
+  // decode segments hold at most max_decode_tokens new tokens each, and all
+  // of them together at most num_tokens
+  l.rows_cap = std::min<int64_t>(num_tokens, (int64_t)num_seqs * max_decode_tokens(hq / hkv));
   size_t off = sizeof(WsHeader);
   l.decode_items = off;
   off = align256(off + (size_t)l.decode_cap * sizeof(int2));
   l.prefill_items = off;
   off = align256(off + (size_t)l.prefill_cap * sizeof(pkv::PrefillItem));
+  l.seg_row = off;
+  off = align256(off + (size_t)num_seqs * sizeof(int32_t));
   l.part_ml = off;
-  off = align256(off + (size_t)l.decode_cap * hq * sizeof(float2));
+  off = align256(off + (size_t)l.rows_cap * l.pmax * hq * sizeof(float2));
   l.part_o = off;
-  off = align256(off + (size_t)l.decode_cap * hq * head_dim * sizeof(float));
+  off = align256(off + (size_t)l.rows_cap * l.pmax * hq * head_dim * sizeof(float));
   l.total = off;
   return l;
 }
@@ -208,7 +219,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
     return fail(PAGED_EINVAL, "paged_attention: scale must be finite");
   const Layout l = layout(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                           max_blocks_per_seq);
-  if (l.decode_cap > INT32_MAX / 64 || l.prefill_cap > INT32_MAX / 64)
+  if (l.decode_cap > INT32_MAX / 64 || l.prefill_cap > INT32_MAX / 64 || l.rows_cap > INT32_MAX / 64)
     return fail(PAGED_EINVAL, "paged_attention: too many work items");
   if (workspace_bytes < l.total)
     return fail(PAGED_EINVAL, "paged_attention: workspace of %zu bytes, %zu needed",
@@ -240,6 +251,9 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   pp.query_tile = query_tile;
   pp.decode_cap = (int32_t)l.decode_cap;
   pp.prefill_cap = (int32_t)l.prefill_cap;
+  pp.seg_row = reinterpret_cast<int32_t*>(ws + l.seg_row);
+  pp.max_decode_n = max_decode_tokens(group);
+  pp.rows_cap = (int32_t)l.rows_cap;
   e = stage(0, stream);
   if (e == hipSuccess) e = launch_plan(pp, stream);
   if (e == hipSuccess) e = stage(1, stream);
@@ -257,6 +271,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   dp.part_ml = reinterpret_cast<float2*>(ws + l.part_ml);
   dp.hdr = hdr;
   dp.items = pp.decode_items;
+  dp.seg_row = pp.seg_row;
   dp.q_stride = q_token_stride;
   dp.num_blocks = num_blocks;
   dp.width = max_blocks_per_seq;

@@ -5,7 +5,10 @@
 // 16-token blocks listed by the segment's block table; its query heads of
 // group g (G = Hq/Hkv of them) attend to all L keys of KV head g.  Decode
 // reads every cached K/V byte once per step, so it is bound by HBM bandwidth
-// ("从0开始的vLLM学习": decode is memory-bandwidth bound).
+// ("从0开始的vLLM学习": decode is memory-bandwidth bound).  A segment of a few
+// new tokens (n * G <= 16: a speculative-decoding check of n - 1 drafted
+// tokens, for instance) is the same read: its n * G query rows share the
+// item, and row (token i, head h) sees keys 0 .. L - n + i.
 //
 // Work split: a work item is (segment, partition of P keys, KV head) and is
 // run by one wavefront; partitions of long contexts run on different waves
@@ -14,9 +17,9 @@
 // the merge rescales by exp(m_p - max_p m_p)).
 //
 // Per wave, per 32 keys (two blocks):
-//   S^T[key, head] = K[key, :] . Q[head, :]     16x16x32 bf16 MFMA, D/32 slabs,
-//                                               Q (zero-padded to 16 heads) in
-//                                               registers for the whole item
+//   S^T[key, row] = K[key, :] . Q[row, :]       16x16x32 bf16 MFMA, D/32 slabs,
+//                                               Q (n * G rows, zero-padded to
+//                                               16) in registers for the item
 //   online softmax in fp32 (exp2 with scale*log2(e) folded in)
 //   O^T[d, head] += V^T[d, key] . P^T[key, head] 16x16x32 bf16 MFMA, D/16 tiles
 // The C layout of the first product (lane = head, 4 keys per lane group) is
@@ -99,7 +102,7 @@ __device__ __forceinline__ void load_kv(KvRegs<D>& r, const BlockRs& b0, const B
 template <int D>
 __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf)[D / 32],
                                             f32x4 (&o)[D / 16], float& m_run, float& l_run,
-                                            int kb, int key1, bool ok0, bool ok1, int j,
+                                            int kb, int kend, bool ok0, bool ok1, int j,
                                             float scale_log2) {
   constexpr int NS = D / 32;
   constexpr int NT = D / 16;
@@ -116,7 +119,7 @@ __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf
   for (int i = 0; i < 8; ++i) {
     const int b = i >> 2;
     const bool okb = b ? ok1 : ok0;
-    const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < key1);
+    const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < kend);
     x[i] = live ? sc[b][i & 3] * scale_log2 : -INFINITY;
     cmax = fmaxf(cmax, x[i]);
   }
@@ -173,14 +176,22 @@ decode_kernel(DecodeParams p) {
     const int part = item.y;
     const int L = p.lens[s];
     const int tok = p.cu[s];
+    const int n = p.cu[s + 1] - tok;
+    const int row0 = p.seg_row[s];   // first partial row of the segment
+    if (row0 < 0) continue;          // skipped by the plan (and flagged there)
     const int key0 = part * p.part_tokens;
     const int key1 = min(L, key0 + p.part_tokens);
     const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
 
-    const bool head_live = m < p.group;
+    // query row m of the item: token ti of the segment, head hh of the group;
+    // it sees the partition's keys below kend (causal within the segment)
+    const int ti = m / p.group;
+    const int hh = m - ti * p.group;
+    const bool head_live = ti < n;
+    const int kend = min(key1, L - n + 1 + ti);
     u32x4 qf[NS];
     {
-      const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride + (int64_t)(g * p.group + m) * D + 8 * j;
+      const uint16_t* qrow = p.q + (int64_t)(tok + ti) * p.q_stride + (int64_t)(g * p.group + hh) * D + 8 * j;
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) {
         u32x4 z = {0u, 0u, 0u, 0u};
@@ -224,23 +235,23 @@ decode_kernel(DecodeParams p) {
         const BlockRs x0 = block_at(kn, 0, bo0), x1 = block_at(kn, 1, bo1);
         load_kv<D>(rb, x0, x1, m, j, (uint32_t)row_bytes);
       }
-      attend_step<D>(ra, qf, o, m_run, l_run, kb, key1, ao0, ao1, j, p.scale_log2);
+      attend_step<D>(ra, qf, o, m_run, l_run, kb, kend, ao0, ao1, j, p.scale_log2);
       if (kn >= key1) break;
       const int kn2 = kb + 64;
       if (kn2 < key1) {
         const BlockRs x0 = block_at(kn2, 0, ao0), x1 = block_at(kn2, 1, ao1);
         load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
       }
-      attend_step<D>(rb, qf, o, m_run, l_run, kn, key1, bo0, bo1, j, p.scale_log2);
+      attend_step<D>(rb, qf, o, m_run, l_run, kn, kend, bo0, bo1, j, p.scale_log2);
     }
 
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     if (head_live) {
-      const int hq = g * p.group + m;
+      const int hq = g * p.group + hh;
       if (nparts == 1) {
         const float inv = 1.f / l_run;
-        uint16_t* orow = p.out + ((int64_t)tok * p.hq + hq) * D;
+        uint16_t* orow = p.out + ((int64_t)(tok + ti) * p.hq + hq) * D;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           uint32_t wv[NT / 2];
@@ -254,7 +265,7 @@ decode_kernel(DecodeParams p) {
           }
         }
       } else {
-        const int64_t slot = ((int64_t)s * p.pmax + part) * p.hq + hq;
+        const int64_t slot = ((int64_t)(row0 + ti) * p.pmax + part) * p.hq + hq;
         float* prow = p.part_o + slot * D;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -270,8 +281,10 @@ decode_kernel(DecodeParams p) {
 }
 
 // Merge of the partitions of every multi-partition decode segment.  One wave
-// per (segment, query head); lanes split d.  The weights exp2(m_p - max m)
-// rescale each partition's sum and output to the common maximum.
+// per (segment, query head), for each of the segment's new tokens; lanes
+// split d.  The weights exp2(m_p - max m) rescale each partition's sum and
+// output to the common maximum (a partition none of whose keys a token sees
+// has m_p = -inf and weight 0; partition 0 always holds key 0).
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
@@ -281,42 +294,46 @@ decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
   const int s = blockIdx.x / hchunks;
   const int hq = (blockIdx.x % hchunks) * 4 + (threadIdx.x >> 6);
   if (s >= num_seqs || hq >= p.hq) return;
+  const int row0 = p.seg_row[s];
+  if (row0 < 0) return;   // not a decode segment (or skipped by the plan)
   const int c0 = p.cu[s];
   const int c1 = p.cu[s + 1];
   const int L = p.lens[s];
-  if (c0 < 0 || c1 > num_tokens || c1 - c0 != 1 || L < 1 || L > p.width * kBlock) return;
+  if (c0 < 0 || c1 > num_tokens || c1 <= c0 || L < c1 - c0 || L > p.width * kBlock) return;
   const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
   if (nparts <= 1) return;
-  const int64_t base = (int64_t)s * p.pmax * p.hq + hq;   // slot of partition 0
-  float mx = -INFINITY;
-  for (int i = lane; i < nparts; i += 64) mx = fmaxf(mx, p.part_ml[base + (int64_t)i * p.hq].x);
+  for (int ti = 0; ti < c1 - c0; ++ti) {
+    const int64_t base = (int64_t)(row0 + ti) * p.pmax * p.hq + hq;   // slot of partition 0
+    float mx = -INFINITY;
+    for (int i = lane; i < nparts; i += 64) mx = fmaxf(mx, p.part_ml[base + (int64_t)i * p.hq].x);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float den = 0.f;
-  for (int i = lane; i < nparts; i += 64) {
-    const float2 ml = p.part_ml[base + (int64_t)i * p.hq];
-    den += ml.x == -INFINITY ? 0.f : ml.y * exp2f(ml.x - mx);
-  }
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float den = 0.f;
+    for (int i = lane; i < nparts; i += 64) {
+      const float2 ml = p.part_ml[base + (int64_t)i * p.hq];
+      den += ml.x == -INFINITY ? 0.f : ml.y * exp2f(ml.x - mx);
+    }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
-  float acc[PER];
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    float acc[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int i = 0; i < nparts; ++i) {
-    const int64_t slot = base + (int64_t)i * p.hq;
-    const float mp = p.part_ml[slot].x;
-    const float w = mp == -INFINITY ? 0.f : exp2f(mp - mx);
-    const float* src = p.part_o + slot * D + lane * PER;
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    for (int i = 0; i < nparts; ++i) {
+      const int64_t slot = base + (int64_t)i * p.hq;
+      const float mp = p.part_ml[slot].x;
+      const float w = mp == -INFINITY ? 0.f : exp2f(mp - mx);
+      const float* src = p.part_o + slot * D + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * src[e];
-  }
-  const float inv = 1.f / den;
-  uint16_t* dst = p.out + ((int64_t)c0 * p.hq + hq) * D + lane * PER;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
-  } else {
-    __bf16 b = (__bf16)(acc[0] * inv);
-    *dst = __builtin_bit_cast(uint16_t, b);
+      for (int e = 0; e < PER; ++e) acc[e] += w * src[e];
+    }
+    const float inv = 1.f / den;
+    uint16_t* dst = p.out + ((int64_t)(c0 + ti) * p.hq + hq) * D + lane * PER;
+    if constexpr (PER == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
+    } else {
+      __bf16 b = (__bf16)(acc[0] * inv);
+      *dst = __builtin_bit_cast(uint16_t, b);
+    }
   }
 }
 

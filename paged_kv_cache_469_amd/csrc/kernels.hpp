@@ -26,6 +26,7 @@ struct PlanParams {
   WsHeader* hdr;
   int2* decode_items;
   PrefillItem* prefill_items;
+  int32_t* seg_row;      // per segment: first partial row of a decode segment, else -1
   int32_t num_seqs;
   int32_t num_tokens;
   int32_t width;         // block-table row length
@@ -34,6 +35,8 @@ struct PlanParams {
   int32_t query_tile;    // QT
   int32_t decode_cap;    // capacity of decode_items
   int32_t prefill_cap;   // capacity of prefill_items
+  int32_t max_decode_n;  // segments with 1 <= n <= this take the decode path
+  int32_t rows_cap;      // partial rows (one per new token of a decode segment)
 };
 
 struct DecodeParams {
@@ -43,8 +46,9 @@ struct DecodeParams {
   const int32_t* cu;
   const int32_t* lens;
   uint16_t* out;
-  float* part_o;           // [S, pmax, Hq, D]
-  float2* part_ml;         // [S, pmax, Hq]  (running max in log2 units, sum)
+  float* part_o;           // [rows, pmax, Hq, D]
+  float2* part_ml;         // [rows, pmax, Hq]  (running max in log2 units, sum)
+  const int32_t* seg_row;  // per segment: its first partial row (token 0), -1 if not decode
   WsHeader* hdr;
   const int2* items;       // (segment, partition)
   int64_t q_stride;

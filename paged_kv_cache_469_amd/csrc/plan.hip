@@ -5,9 +5,13 @@
 //
 // One workgroup of 1024 threads walks the segments on the device, so the
 // host never reads metadata and the whole call can be captured in a graph:
-//   n == 1 -> decode: ceil(L / P) items (segment, partition)
-//   n >  1 -> prefill: ceil(n / QT) items (segment, query tile), each with
-//             the segment bounds and its first eight block ids
+//   1 <= n <= N_dec -> decode: ceil(L / P) items (segment, partition); the
+//             segment's n tokens get n consecutive rows of partial results
+//             (seg_row[s] is the first), n * G <= 16 query rows per KV head
+//             (one decode step, or a few tokens of a speculative-decoding
+//             check, over a long history)
+//   n >  N_dec -> prefill: ceil(n / QT) items (segment, query tile), each
+//             with the segment bounds and its first eight block ids
 //   n == 0 -> nothing
 // Prefill items are ordered by their number of 64-key tiles, most first (a
 // counting sort over 1024 cost buckets), so the dynamic queues hand out the
@@ -82,25 +86,37 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   if (threadIdx.x < 16) p.hdr->zeros[threadIdx.x] = 0u;
   __syncthreads();
 
-  // pass 1: decode items in segment order; prefill item count and cost histogram
+  // pass 1: decode items and partial rows in segment order; prefill item
+  // count and cost histogram
   int dec_base = 0;
+  int row_base = 0;
   int pre_total = 0;
   uint32_t status = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
     const SegInfo si = seg_info(p, s);
-    int nd = 0, np = 0;
+    int nd = 0, np = 0, nr = 0;
     if (s < p.num_seqs && !si.ok) {
       status |= 1u;
-    } else if (si.ok && si.n == 1) {
+    } else if (si.ok && si.n >= 1 && si.n <= p.max_decode_n) {
       nd = (si.L + p.part_tokens - 1) / p.part_tokens;
-    } else if (si.ok && si.n > 1) {
+      nr = si.n;
+    } else if (si.ok && si.n > p.max_decode_n) {
       np = (si.n + p.query_tile - 1) / p.query_tile;
       for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
     }
-    int tot_d, tot_p;
+    int tot_d, tot_p, tot_r;
     const int od = dec_base + block_exclusive_scan(nd, scratch, &tot_d);
     block_exclusive_scan(np, scratch, &tot_p);
+    const int orow = row_base + block_exclusive_scan(nr, scratch, &tot_r);
+    if (s < p.num_seqs) {
+      // rows past the capacity (only possible with overlapping segments):
+      // the segment is skipped by the decode kernels and flagged
+      const bool fits = nr > 0 && orow + nr <= p.rows_cap;
+      p.seg_row[s] = fits ? orow : -1;
+      if (nr > 0 && !fits) status |= 1u;
+    }
+    row_base += tot_r;
     // overlapping segments (only possible when some segment is malformed)
     // could overflow the lists: items past the capacity are dropped and flagged
     for (int i = 0; i < nd; ++i)
@@ -122,7 +138,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     for (int base = 0; base < p.num_seqs; base += 1024) {
       const int s = base + (int)threadIdx.x;
       const SegInfo si = seg_info(p, s);
-      if (si.ok && si.n > 1) {
+      if (si.ok && si.n > p.max_decode_n) {
         const int np = (si.n + p.query_tile - 1) / p.query_tile;
         PrefillItem it{};
         it.seq = s;

@@ -104,6 +104,54 @@ def test_partition_sizes(tokens):
     check_close(out[rows], np.concatenate([x for _, x in refs.values()]), f"P={tokens}")
 
 
+# Segments of a few new tokens over a history (one decode step, or a
+# speculative-decoding check of n - 1 drafted tokens) take the split-context
+# decode path when n * G <= 16 and n <= 8, beside longer segments on the
+# prefill path.  Small partitions give many partials per token, including
+# last partitions none of whose keys some of the segment's tokens see.
+MULTI = [
+    ("g4_d128", dict(hq=32, hkv=8, d=128, segs=[(1, 97), (2, 2), (2, 1025), (3, 67), (4, 4),
+                                               (4, 4097), (4, 3001), (3, 2050), (5, 700)])),
+    ("g1_d64", dict(hq=8, hkv=8, d=64, segs=[(8, 8), (8, 2000), (7, 333), (6, 1024), (1, 1),
+                                            (9, 40)])),
+    ("g2_d128", dict(hq=16, hkv=8, d=128, segs=[(8, 1500), (2, 2), (5, 4100), (9, 9)])),
+    ("g8_d64", dict(hq=32, hkv=4, d=64, segs=[(2, 2), (2, 3333), (1, 50), (3, 600)])),
+    ("g3_d128", dict(hq=6, hkv=2, d=128, segs=[(5, 800), (4, 4), (2, 2049), (6, 90)])),
+]
+
+
+@pytest.mark.parametrize("tokens", [32, 256, 0])
+@pytest.mark.parametrize("name,kw", MULTI, ids=[m[0] for m in MULTI])
+def test_multi_token_decode(name, kw, tokens):
+    wl = _custom(kw["hq"], kw["hkv"], kw["d"], kw["segs"], cfg=51, num_blocks=None)
+    log(f"case multi-token decode {name} P={tokens}")
+    pkv.paged_attention_set_partition_tokens(tokens)
+    try:
+        st = DeviceStep(wl, host_pool=True)
+        out = down_u16(st.attend())
+    finally:
+        pkv.paged_attention_set_partition_tokens(0)
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens,
+                       wl.scale)
+    check_close(out, ref, f"{name} P={tokens}")
+    assert st.status() == 0
+
+
+def test_multi_token_decode_sharpened():
+    kw = MULTI[0][1]
+    wl = _custom(kw["hq"], kw["hkv"], kw["d"], kw["segs"], cfg=51, num_blocks=None)
+    log("case multi-token decode sharpened")
+    pkv.paged_attention_set_partition_tokens(64)
+    try:
+        st = DeviceStep(wl, host_pool=True, q_gain=4.0)
+        out = down_u16(st.attend())
+    finally:
+        pkv.paged_attention_set_partition_tokens(0)
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens,
+                       wl.scale)
+    check_close(out, ref, "multi-token sharpened")
+
+
 def test_permutation_invariance_and_determinism():
     kw = dict(num_decodes=10, ctx=(1024, 2500), shared=3, prefix=1024, chunk=130, chunk_history=300)
     a = workloads.make("cb_step_8b", **kw)
@@ -253,3 +301,11 @@ def test_full_long_decode_70b():
         f"KV {wl.kv_bytes_logical() / 1e9:.1f} GB")
     got, ref = _full_sampled(wl, [3, 40], pool_blocks=nb, fill_others=True)
     check_close(got, ref, "long_decode_70b full (2 sampled requests)")
+
+
+def test_full_spec_verify_8b():
+    wl = workloads.make("spec_verify_8b")
+    log(f"case full spec_verify_8b: KV {wl.kv_bytes_logical() / 1e9:.2f} GB")
+    sample = np.random.default_rng(3).choice(wl.num_seqs, 8, replace=False)
+    got, ref = _full_sampled(wl, sample, fill_others=True)
+    check_close(got, ref, "spec_verify_8b full (8 sampled requests)")

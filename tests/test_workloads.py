@@ -50,6 +50,7 @@ def _check_slots_cover(wl):
     ("cb_step_8b", {"num_decodes": 6, "ctx": (40, 90), "shared": 3, "prefix": 32,
                     "chunk": 20, "chunk_history": 48, "decode_first": False}),
     ("long_decode_70b", {"num_requests": 3, "ctx": (100, 300), "num_blocks": 5000}),
+    ("spec_verify_8b", {"num_requests": 5, "ctx": (30, 90)}),
 ])
 def test_structure(name, kw):
     wl = workloads.make(name, **kw)

@@ -5,7 +5,9 @@ The shapes follow the workloads the pages describe: a mixed step with a
 01", section 1.6), decode batches over long cached contexts, prompts packed
 end to end, a continuous-batching step under a token budget with one chunk of
 a long prompt (section 2.1) and requests that share a cached system-prompt
-prefix (section 2.2), and a pool sized to a fraction of free device memory.
+prefix (section 2.2), a speculative-decoding check of a few drafted tokens
+per request (section 2.4), and a pool sized to a fraction of free device
+memory.
 
 Every random draw comes from ``np.random.default_rng([469, cfg, purpose,
 idx])`` with purpose 0 = lengths, 1 = block placement, 2 = q, 3 = k/v of
@@ -308,12 +310,23 @@ def long_decode_70b(num_requests=64, ctx=(32768, 131072), **kw):
     return build("long_decode_70b", 5, 64, 8, 128, [(1, int(x) + 1) for x in c], **kw)
 
 
+def spec_verify_8b(num_requests=128, drafts=3, ctx=(2048, 16384), **kw):
+    """8B-shaped speculative-decoding check ("vLLM 学习笔记 01", section 2.4:
+    k drafted tokens are checked by the large model in one forward pass):
+    each request feeds its last accepted token and ``drafts`` drafted ones
+    (n = drafts + 1 new tokens) over a cached context uniform in ``ctx``."""
+    c = _rng(6, 0).integers(ctx[0], ctx[1] + 1, size=num_requests)
+    n = drafts + 1
+    return build("spec_verify_8b", 6, 32, 8, 128, [(n, int(x) + n) for x in c], **kw)
+
+
 NAMED = {
     "tiny_mixed": tiny_mixed,
     "decode_8b": decode_8b,
     "prefill_8b": prefill_8b,
     "cb_step_8b": cb_step_8b,
     "long_decode_70b": long_decode_70b,
+    "spec_verify_8b": spec_verify_8b,
 }
 
 
