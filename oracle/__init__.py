@@ -24,10 +24,13 @@ Modules:
 * ``bf16``   -- bf16 <-> float bit helpers (numpy has no bf16 dtype here).
 * ``paged``  -- the oracle proper: block bytes, write, gather, attention (fp64).
 * ``brute``  -- a scalar pure-Python twin of the attention, for tiny inputs.
+* ``block_manager`` -- a plain list/dict model of the KV block manager (free
+  queue, reference counts, prefix cache, slot allocation), sections 1.4, 1.5
+  and 2.2 of [NOTES01].
 
 Every function is a plain definition: no blocking, fusion or reordering
 beyond what the definition states.  Parity status of each function is given
 in its docstring; every function here is pinned by ``tests/test_oracle_*.py``.
 """
 
-from . import bf16, brute, paged  # noqa: F401
+from . import bf16, block_manager, brute, paged  # noqa: F401

@@ -24,3 +24,4 @@ from ._lib import (  # noqa: F401
     STATUS_BAD_BLOCK,
     STATUS_BAD_SEGMENT,
 )
+from .block_manager import BlockManager, BlockManagerError  # noqa: F401,E402

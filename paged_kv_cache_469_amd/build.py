@@ -1,8 +1,9 @@
 """Build the HIP library ``libpaged_attn.so`` in-tree for gfx950.
 
-Every ``csrc/*.hip`` file is compiled with hipcc (in parallel) and linked
-into one shared library next to this file.  Packed-FP32 instructions are
-switched off for all device code.
+Every ``csrc/*.hip`` file is compiled with hipcc and every ``csrc/*.cpp``
+file (host-only C++: the block manager) with g++, in parallel, and all are
+linked into one shared library next to this file.  Packed-FP32 instructions
+are switched off for all device code.
 """
 
 import concurrent.futures
@@ -42,9 +43,15 @@ def _hipcc():
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [shutil.which("g++") or "g++", *HOST_FLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [_hipcc(), *FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -53,7 +60,7 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(OBJ, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"

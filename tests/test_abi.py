@@ -1,22 +1,24 @@
 """CPU checks of the C ABI: the library loads, exports every symbol that
-include/paged_attn.h declares, and its pure and argument-checking paths
+the headers under include/ declare, and its pure and argument-checking paths
 behave (no GPU work is started here)."""
 
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(paged_[a-z_0-9]+)\s*\(", text)
-    return sorted(set(names))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(paged_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +32,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("paged_kv_write", "paged_attention", "paged_attention_workspace_size",
-                 "paged_kv_block_bytes", "paged_validate", "paged_last_error"):
+                 "paged_kv_block_bytes", "paged_validate", "paged_last_error",
+                 "paged_bm_create", "paged_bm_allocate_slots", "paged_bm_step_metadata"):
         assert want in names
 
 
