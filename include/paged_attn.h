@@ -116,6 +116,26 @@ int paged_attention(const void* q, const void* kv_cache,
                     int32_t max_blocks_per_seq, int64_t q_token_stride,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Metadata of a steady-state decode step, on the device ([NOTES01] sections
+ * 1.4 and 1.6): every one of the num_seqs segments gains one new token at
+ * position L = seq_lens[s] (its current length).  In place on `stream`:
+ *   seq_lens[s]      = L + 1
+ *   cu_seqlens_q[s]  = s, cu_seqlens_q[num_seqs] = num_seqs
+ *   slot_mapping[s]  = block_tables[s][L / 16] * 16 + L % 16, or -1 when
+ *                      L / 16 >= max_blocks_per_seq or that entry is outside
+ *                      [0, num_blocks) (paged_kv_write then skips the token
+ *                      and paged_attention flags the block).
+ * The caller keeps each table holding the blocks of the positions to come
+ * (a block manager allocates them ahead).  With it, a decode step --
+ * paged_decode_advance, paged_kv_write, paged_attention -- reads no host
+ * metadata and can be captured once in a HIP graph and replayed.  All
+ * pointers are device pointers: seq_lens, cu_seqlens_q ([num_seqs + 1]) and
+ * slot_mapping ([num_seqs]) are written; block_tables is read.  No
+ * allocation, no synchronisation. */
+int paged_decode_advance(int32_t* seq_lens, int32_t* cu_seqlens_q, int32_t* slot_mapping,
+                         const int32_t* block_tables, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, hipStream_t stream);
+
 /* Debug check of the metadata preconditions of paged_kv_write and
  * paged_attention.  Synchronises `stream`, copies the index arrays to the
  * host and returns PAGED_OK or PAGED_EINVAL with the first violation in

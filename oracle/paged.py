@@ -38,7 +38,8 @@ What is computed, and where the pages state it:
 
 Parity status: every function below is pinned (``tests/test_oracle_*.py``):
 block bytes by the page's closed form; write by round trips and poison
-checks; attention by brute force on tiny inputs, by closed forms (single key,
+checks; the decode-step metadata by the block-manager model's slots for a
+decode token and by its out-of-table and out-of-pool cases; attention by brute force on tiny inputs, by closed forms (single key,
 zero query, index-valued V, head-valued V, two-key logistic form, one
 dominant key) and by the invariants paged == dense, block permutation,
 shared prefix == private copies, segment isolation, decode == last row of a
@@ -88,6 +89,28 @@ def kv_write(k, v, slot_mapping, pool):
         pool[b, 0, r] = k[t]
         pool[b, 1, r] = v[t]
     return pool
+
+
+def decode_advance(block_tables, seq_lens, num_blocks):
+    """Metadata of a decode step in which every segment gains one token
+    ([NOTES01] sections 1.4 and 1.6).  The new token of segment s sits at
+    position L = seq_lens[s]; returns (seq_lens + 1, cu_seqlens_q = 0..S,
+    slot_mapping) with slot = table[s][L // 16] * 16 + L % 16, or -1 when
+    that entry is past the table or outside [0, num_blocks)."""
+    tables = np.asarray(block_tables, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    s_count, width = tables.shape
+    slots = []
+    for s in range(s_count):
+        pos = int(lens[s])
+        slot = -1
+        if 0 <= pos and pos // BLOCK_SIZE < width:
+            b = int(tables[s, pos // BLOCK_SIZE])
+            if 0 <= b < num_blocks:
+                slot = b * BLOCK_SIZE + pos % BLOCK_SIZE
+        slots.append(slot)
+    return ((lens + 1).astype(np.int32), np.arange(s_count + 1, dtype=np.int32),
+            np.array(slots, dtype=np.int32))
 
 
 def gather(pool, table_row, length):

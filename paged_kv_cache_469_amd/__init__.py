@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     paged_attention_set_partition_tokens,
     paged_attention_set_stage_events,
     paged_attention_workspace_size,
+    paged_decode_advance,
     paged_kv_block_bytes,
     paged_kv_write,
     paged_last_error,

@@ -30,6 +30,7 @@ _SIGS = {
     "paged_attention_device_status": (_c_i32, [_c_p, ctypes.POINTER(ctypes.c_uint32), _c_p]),
     "paged_attention_set_partition_tokens": (_c_i32, [_c_i32]),
     "paged_attention_set_stage_events": (_c_i32, [ctypes.POINTER(_c_p), _c_i32]),
+    "paged_decode_advance": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i64, _c_p]),
     "paged_last_error": (ctypes.c_char_p, []),
 }
 
@@ -199,3 +200,24 @@ def paged_attention_set_stage_events(events):
         handles.append(e.cuda_event)
     arr = (_c_p * len(handles))(*handles)
     _check(lib().paged_attention_set_stage_events(arr, len(handles)))
+
+
+def paged_decode_advance(block_tables, seq_lens, cu_seqlens_q, slot_mapping, num_blocks,
+                         stream=None):
+    """One decode token per segment, metadata on the device: seq_lens += 1,
+    cu_seqlens_q = 0..S, slot_mapping[s] = the new token's slot (int32 CUDA
+    tensors, updated in place)."""
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    s, w = block_tables.shape
+    if seq_lens.shape != (s,) or cu_seqlens_q.shape != (s + 1,) or slot_mapping.shape != (s,):
+        raise ValueError("seq_lens [S], cu_seqlens_q [S+1], slot_mapping [S] for block_tables [S, W]")
+    for t, nm in ((block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                  (cu_seqlens_q, "cu_seqlens_q"), (slot_mapping, "slot_mapping")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    _check(lib().paged_decode_advance(seq_lens.data_ptr(), cu_seqlens_q.data_ptr(),
+                                      slot_mapping.data_ptr(), block_tables.data_ptr(), s, w,
+                                      int(num_blocks), _stream(stream)))

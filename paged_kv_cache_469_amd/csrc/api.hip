@@ -323,6 +323,20 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   return PAGED_OK;
 }
 
+int paged_decode_advance(int32_t* seq_lens, int32_t* cu_seqlens_q, int32_t* slot_mapping,
+                         const int32_t* block_tables, int32_t num_seqs,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, hipStream_t stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return fail(PAGED_EINVAL, "paged_decode_advance: negative size");
+  if (!cu_seqlens_q) return fail(PAGED_EINVAL, "paged_decode_advance: null pointer");
+  if (num_seqs > 0 && (!seq_lens || !slot_mapping || !block_tables))
+    return fail(PAGED_EINVAL, "paged_decode_advance: null pointer");
+  hipError_t e = launch_decode_advance(seq_lens, cu_seqlens_q, slot_mapping, block_tables,
+                                       num_seqs, max_blocks_per_seq, num_blocks, stream);
+  if (e != hipSuccess) return fail_hip(e, "paged_decode_advance launch");
+  return PAGED_OK;
+}
+
 int paged_validate(const int32_t* slot_mapping, int32_t num_new_tokens,
                    const int32_t* block_tables, const int32_t* cu_seqlens_q,
                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_tokens,

@@ -86,6 +86,9 @@ hipError_t launch_kv_write(const void* k, const void* v, const int32_t* slots, v
                            int64_t num_blocks, int64_t k_stride, int64_t v_stride,
                            hipStream_t stream);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_decode_advance(int32_t* seq_lens, int32_t* cu, int32_t* slots, const int32_t* bt,
+                                 int32_t num_seqs, int32_t width, int64_t num_blocks,
+                                 hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeParams& p, int head_dim, int num_seqs, int num_tokens,
                                hipStream_t stream);

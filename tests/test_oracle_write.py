@@ -99,3 +99,45 @@ def test_write_all_skipped_is_noop():
     k = np.ones((4, 1, 2), dtype=np.uint16)
     paged.kv_write(k, k, np.full(4, -1, dtype=np.int32), pool)
     assert np.all(pool == 7)
+
+
+def test_decode_advance_matches_block_manager_model():
+    # the slot of each new decode token, from the block-manager model's own
+    # allocation (an independent computation of block * 16 + position)
+    from oracle.block_manager import BlockManagerModel
+    rng = np.random.default_rng([469, 65, 0])
+    m = BlockManagerModel(200, prefix_caching=False)
+    lens = [int(x) for x in rng.integers(1, 120, size=9)]
+    for r, n in enumerate(lens):
+        m.add_request(r, [0] * n)
+        m.allocate_slots(r, n)
+    for _ in range(40):
+        width = max(len(m.block_table(r)) for r in range(9)) + 1
+        tables = np.full((9, width), -1, dtype=np.int32)
+        for r in range(9):
+            t = m.block_table(r)
+            tables[r, :len(t)] = t
+        want = []
+        for r in range(9):
+            m.append_tokens(r, [0])
+            want += m.allocate_slots(r, 1)
+        # the model took any new block already; the table above may lack it:
+        # refresh the table with the model's blocks first, as a caller would
+        for r in range(9):
+            t = m.block_table(r)
+            tables[r, :len(t)] = t
+        new_lens, cu, slots = paged.decode_advance(tables, lens, 200)
+        assert slots.tolist() == want
+        assert cu.tolist() == list(range(10)) and new_lens.tolist() == [x + 1 for x in lens]
+        lens = new_lens.tolist()
+
+
+def test_decode_advance_edges():
+    tables = np.array([[3, -1], [5, 7], [1, 2]], dtype=np.int32)
+    lens, cu, slots = paged.decode_advance(tables, [16, 31, 32], num_blocks=6)
+    # segment 0: position 16 -> entry 1 = -1; segment 1: position 31 -> block 7
+    # is outside a 6-block pool; segment 2: position 32 is past the table
+    assert slots.tolist() == [-1, -1, -1]
+    lens, cu, slots = paged.decode_advance(tables, [15, 17, 0], num_blocks=8)
+    assert slots.tolist() == [3 * 16 + 15, 7 * 16 + 1, 1 * 16 + 0]
+    assert lens.tolist() == [16, 18, 1] and cu.tolist() == [0, 1, 2, 3]
