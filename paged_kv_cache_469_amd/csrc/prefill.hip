@@ -423,8 +423,10 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   // or past every key its queries see) has P = 0, and every slot read holds
   // finite values, so the extra products change nothing.
   PKV_LDS char* const v_prev = (t & 1) ? sl.v[0] : sl.v[1];   // V slot of tiles t - 1 and t + 1
-  qk<D>(sc, q, ak, sl.k[RK]);
-  pv<D>(o, pr, av, v_prev);
+  // the first step has no P yet and the last one no tile to score: those
+  // products are skipped (wave-uniform branches)
+  if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
+  if (t > 0) pv<D>(o, pr, av, v_prev);
   if (!group_b) {
     // after the products are issued, while the last of them run
     const int bk = 4 * (t + 2) + wq;   // block of K(t+2)
