@@ -13,9 +13,11 @@
 //   n >  N_dec -> prefill: ceil(n / QT) items (segment, query tile), each
 //             with the segment bounds and its first eight block ids
 //   n == 0 -> nothing
-// Prefill items are ordered by their number of 64-key tiles, most first (a
-// counting sort over 1024 cost buckets), so the dynamic queues hand out the
-// longest work first and the short items fill the tail.  Segments whose
+// Both lists are ordered longest work first, so the dynamic queues hand out
+// the long items first and the short ones fill the tail: prefill items by
+// their number of 64-key tiles (a counting sort over 1024 cost buckets),
+// decode items by their keys (full partitions first, then the partial last
+// partitions of the segments by decreasing length, in 32-key buckets).  Segments whose
 // bounds are out of range are skipped and flagged.  The kernel also resets
 // the status word and the dynamic-scheduling counters and writes the zero
 // line of the header, so the workspace needs no clearing between calls.
@@ -56,17 +58,18 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
 }
 
 struct SegInfo {
-  int n, L;
+  int n, L, c0;
   bool ok;
 };
 
 __device__ __forceinline__ SegInfo seg_info(const PlanParams& p, int s) {
-  SegInfo r{0, 0, false};
+  SegInfo r{0, 0, 0, false};
   if (s >= p.num_seqs) return r;
   const int c0 = p.cu[s];
   const int c1 = p.cu[s + 1];
   r.L = p.lens[s];
   r.n = c1 - c0;
+  r.c0 = c0;
   r.ok = c0 >= 0 && c1 <= p.num_tokens && r.n >= 0 && r.L >= r.n && r.L <= p.max_len;
   return r;
 }
@@ -79,10 +82,20 @@ __device__ __forceinline__ int cost_key(int n, int L, int qt, int qtile) {
   return kCostBuckets - 1 - min(tiles, kCostBuckets - 1);
 }
 
+// Bucket of a segment's partial last partition of `keys` keys (1 .. P - 1):
+// one bucket per 32 keys fewer than P, after bucket 0, which holds the full
+// partitions (placed by a scan, in segment order).
+__device__ __forceinline__ int decode_bucket(int keys, int part_tokens) {
+  return 1 + (part_tokens - keys) / 32;
+}
+constexpr int kDecodeBuckets = 1024 / 32 + 2;
+
 __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   __shared__ int scratch[17];
   __shared__ int hist[kCostBuckets];
+  __shared__ int dhist[kDecodeBuckets];
   hist[threadIdx.x] = 0;   // blockDim.x == kCostBuckets
+  if (threadIdx.x < kDecodeBuckets) dhist[threadIdx.x] = 0;
   if (threadIdx.x < 16) p.hdr->zeros[threadIdx.x] = 0u;
   __syncthreads();
 
@@ -92,21 +105,31 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   int row_base = 0;
   int pre_total = 0;
   uint32_t status = 0;
+  SegInfo first{0, 0, 0, false};   // the thread's segment of the first 1024, kept for the later passes
+  int first_ofull = 0;              // and the place of its first full decode partition
+  int full_base = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
     const SegInfo si = seg_info(p, s);
+    if (base == 0) first = si;
     int nd = 0, np = 0, nr = 0;
     if (s < p.num_seqs && !si.ok) {
       status |= 1u;
     } else if (si.ok && si.n >= 1 && si.n <= p.max_decode_n) {
       nd = (si.L + p.part_tokens - 1) / p.part_tokens;
       nr = si.n;
+      if (nd * p.part_tokens > si.L)
+        atomicAdd(&dhist[decode_bucket(si.L - (nd - 1) * p.part_tokens, p.part_tokens)], 1);
     } else if (si.ok && si.n > p.max_decode_n) {
       np = (si.n + p.query_tile - 1) / p.query_tile;
       for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
     }
-    int tot_d, tot_p, tot_r;
-    const int od = dec_base + block_exclusive_scan(nd, scratch, &tot_d);
+    int tot_d, tot_p, tot_r, tot_f;
+    block_exclusive_scan(nd, scratch, &tot_d);
+    const int nfull = nd > 0 ? si.L / p.part_tokens : 0;
+    const int ofull = full_base + block_exclusive_scan(nfull, scratch, &tot_f);
+    if (base == 0) first_ofull = ofull;
+    full_base += tot_f;
     block_exclusive_scan(np, scratch, &tot_p);
     const int orow = row_base + block_exclusive_scan(nr, scratch, &tot_r);
     if (s < p.num_seqs) {
@@ -117,33 +140,64 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       if (nr > 0 && !fits) status |= 1u;
     }
     row_base += tot_r;
-    // overlapping segments (only possible when some segment is malformed)
-    // could overflow the lists: items past the capacity are dropped and flagged
-    for (int i = 0; i < nd; ++i)
-      if (od + i < p.decode_cap) p.decode_items[od + i] = make_int2(s, i);
-    if (od + nd > p.decode_cap) status |= 1u;
     dec_base += tot_d;
     pre_total += tot_p;
   }
   if (pre_total > p.prefill_cap) status |= 1u;
+  // overlapping segments (only possible when some segment is malformed)
+  // could overflow the lists: items past the capacity are dropped and flagged
+  if (dec_base > p.decode_cap) status |= 1u;
   __syncthreads();
 
-  // pass 2: bucket offsets (exclusive scan of the histogram)
+  // pass 2: bucket offsets (exclusive scans of the histograms)
   int unused;
   hist[threadIdx.x] = block_exclusive_scan(hist[threadIdx.x], scratch, &unused);
+  if (threadIdx.x == 0) {
+    dhist[0] = full_base;
+    int run = 0;
+    for (int b = 0; b < kDecodeBuckets; ++b) {
+      const int c = dhist[b];
+      dhist[b] = run;
+      run += c;
+    }
+  }
   __syncthreads();
 
-  // pass 3: scatter prefill items to their bucket's next place
+  // pass 3a: decode items: a segment's full partitions at their scanned
+  // places, its partial last one at its bucket's next place
+  full_base = 0;
+  for (int base = 0; base < p.num_seqs; base += 1024) {
+    const int s = base + (int)threadIdx.x;
+    const SegInfo si = base == 0 ? first : seg_info(p, s);
+    const bool dec = si.ok && si.n >= 1 && si.n <= p.max_decode_n;
+    const int full = dec ? si.L / p.part_tokens : 0;
+    int at = first_ofull;
+    if (base > 0) {   // more than 1024 segments: place the full partitions again
+      int tot_f;
+      at = full_base + block_exclusive_scan(full, scratch, &tot_f);
+      full_base += tot_f;
+    }
+    if (dec) {
+      for (int i = 0; i < full; ++i)
+        if (at + i < p.decode_cap) p.decode_items[at + i] = make_int2(s, i);
+      if (si.L > full * p.part_tokens) {
+        const int at2 = atomicAdd(&dhist[decode_bucket(si.L - full * p.part_tokens, p.part_tokens)], 1);
+        if (at2 < p.decode_cap) p.decode_items[at2] = make_int2(s, full);
+      }
+    }
+  }
+
+  // pass 3b: prefill items to their bucket's next place
   if (pre_total > 0) {
     for (int base = 0; base < p.num_seqs; base += 1024) {
       const int s = base + (int)threadIdx.x;
-      const SegInfo si = seg_info(p, s);
+      const SegInfo si = base == 0 ? first : seg_info(p, s);
       if (si.ok && si.n > p.max_decode_n) {
         const int np = (si.n + p.query_tile - 1) / p.query_tile;
         PrefillItem it{};
         it.seq = s;
         it.L = si.L;
-        it.tok0 = p.cu[s];
+        it.tok0 = si.c0;
         it.n = si.n;
         const int32_t* bt_row = p.bt + (int64_t)s * p.width;
         const int nblk = (si.L + kBlock - 1) / kBlock;   // >= 1: L >= n > 1
