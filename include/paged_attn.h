@@ -98,7 +98,8 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
  * int32 [num_seqs, max_blocks_per_seq] row-major; entries past ceil(L/16) are
  * never read.  cu_seqlens_q: int32 [num_seqs + 1], non-decreasing from 0 to
  * at most num_tokens.  seq_lens: int32 [num_seqs] with n <= L <=
- * max_blocks_per_seq * 16.  Segments with n = 0 are skipped; rows of out that
+ * max_blocks_per_seq * 16.  PAGED_EINVAL when num_tokens / 32 + num_seqs
+ * reaches 2^20 (about 33 M tokens in one call).  Segments with n = 0 are skipped; rows of out that
  * belong to no segment are left untouched.  The K/V pool is read only at
  * (block, position) pairs below each L.  out must not alias q or kv_cache.
  *

@@ -219,7 +219,8 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
     return fail(PAGED_EINVAL, "paged_attention: scale must be finite");
   const Layout l = layout(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                           max_blocks_per_seq);
-  if (l.decode_cap > INT32_MAX / 64 || l.prefill_cap > INT32_MAX / 64 || l.rows_cap > INT32_MAX / 64)
+  // the plan kernel counts prefill items in 20 bits
+  if (l.decode_cap > INT32_MAX / 64 || l.prefill_cap >= (1 << 20) || l.rows_cap > INT32_MAX / 64)
     return fail(PAGED_EINVAL, "paged_attention: too many work items");
   if (workspace_bytes < l.total)
     return fail(PAGED_EINVAL, "paged_attention: workspace of %zu bytes, %zu needed",

@@ -94,6 +94,13 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   __shared__ int scratch[17];
   __shared__ int hist[kCostBuckets];
   __shared__ int dhist[kDecodeBuckets];
+  // prefill segments of a batch of at most 1024 segments, listed so that one
+  // wave per segment spreads its query tiles over the lanes
+  __shared__ int pl_seg[1024], pl_n[1024], pl_len[1024], pl_c0[1024];
+  __shared__ int pl_count;
+  const bool one_chunk = p.num_seqs <= 1024;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   hist[threadIdx.x] = 0;   // blockDim.x == kCostBuckets
   if (threadIdx.x < kDecodeBuckets) dhist[threadIdx.x] = 0;
   if (threadIdx.x < 16) p.hdr->zeros[threadIdx.x] = 0u;
@@ -122,7 +129,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
         atomicAdd(&dhist[decode_bucket(si.L - (nd - 1) * p.part_tokens, p.part_tokens)], 1);
     } else if (si.ok && si.n > p.max_decode_n) {
       np = (si.n + p.query_tile - 1) / p.query_tile;
-      for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
+      if (!one_chunk)
+        for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
     }
     int tot_d, tot_p, tot_r, tot_f;
     block_exclusive_scan(nd, scratch, &tot_d);
@@ -130,7 +138,20 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     const int ofull = full_base + block_exclusive_scan(nfull, scratch, &tot_f);
     if (base == 0) first_ofull = ofull;
     full_base += tot_f;
-    block_exclusive_scan(np, scratch, &tot_p);
+    // one scan counts the prefill items (low 20 bits: fewer than 2^20 per
+    // call) and places the prefill segments in the list (bits 20 and up)
+    const int packed = block_exclusive_scan(np + (np > 0 ? 1 << 20 : 0), scratch, &tot_p);
+    if (one_chunk) {
+      if (np > 0) {
+        const int k = packed >> 20;
+        pl_seg[k] = s;
+        pl_n[k] = si.n;
+        pl_len[k] = si.L;
+        pl_c0[k] = si.c0;
+      }
+      if (threadIdx.x == 0) pl_count = tot_p >> 20;
+    }
+    tot_p &= (1 << 20) - 1;
     const int orow = row_base + block_exclusive_scan(nr, scratch, &tot_r);
     if (s < p.num_seqs) {
       // rows past the capacity (only possible with overlapping segments):
@@ -148,6 +169,14 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   // could overflow the lists: items past the capacity are dropped and flagged
   if (dec_base > p.decode_cap) status |= 1u;
   __syncthreads();
+  if (one_chunk && pl_count > 0) {   // pass 1b: the cost histogram, one wave per prefill segment
+    for (int k = wave; k < pl_count; k += 16) {
+      const int n = pl_n[k], L = pl_len[k];
+      const int np = (n + p.query_tile - 1) / p.query_tile;
+      for (int qt = lane; qt < np; qt += 64) atomicAdd(&hist[cost_key(n, L, qt, p.query_tile)], 1);
+    }
+    __syncthreads();
+  }
 
   // pass 2: bucket offsets (exclusive scans of the histograms)
   int unused;
@@ -188,7 +217,29 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   }
 
   // pass 3b: prefill items to their bucket's next place
-  if (pre_total > 0) {
+  if (pre_total > 0 && one_chunk) {
+    // one wave per prefill segment: lanes 0-7 read its first eight block ids,
+    // every lane writes the descriptors of query tiles lane, lane + 64, ...
+    for (int k = wave; k < pl_count; k += 16) {
+      const int s = pl_seg[k], n = pl_n[k], L = pl_len[k];
+      const int np = (n + p.query_tile - 1) / p.query_tile;
+      const int nblk = (L + kBlock - 1) / kBlock;   // >= 1: L >= n > 1
+      int bid = 0;
+      if (lane < 8) bid = p.bt[(int64_t)s * p.width + min(lane, nblk - 1)];
+      PrefillItem it{};
+      it.seq = s;
+      it.L = L;
+      it.tok0 = pl_c0[k];
+      it.n = n;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) it.bid[j] = __shfl(bid, j);
+      for (int qt = lane; qt < np; qt += 64) {
+        const int at = atomicAdd(&hist[cost_key(n, L, qt, p.query_tile)], 1);
+        it.qt = qt;
+        if (at < p.prefill_cap) p.prefill_items[at] = it;
+      }
+    }
+  } else if (pre_total > 0) {
     for (int base = 0; base < p.num_seqs; base += 1024) {
       const int s = base + (int)threadIdx.x;
       const SegInfo si = base == 0 ? first : seg_info(p, s);
