@@ -418,13 +418,11 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   constexpr int RP = (R + 2) % 3;   // K slot of tiles t - 1 and t + 2
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
   const int wq = wave & 3;
-  // Matrix phase: QK(t) and PV(t-1) run on every step, as one scheduling
-  // region.  A tile the wave does not use (before the first, past the last,
-  // or past every key its queries see) has P = 0, and every slot read holds
-  // finite values, so the extra products change nothing.
+  // Matrix phase: QK(t) and PV(t-1), except that the first step has no P
+  // yet and the last one no tile to score (wave-uniform branches).  A tile
+  // the wave's queries do not see (past every key they see) has P = 0, and
+  // every slot read holds finite values, so its products change nothing.
   PKV_LDS char* const v_prev = (t & 1) ? sl.v[0] : sl.v[1];   // V slot of tiles t - 1 and t + 1
-  // the first step has no P yet and the last one no tile to score: those
-  // products are skipped (wave-uniform branches)
   if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
   if (t > 0) pv<D>(o, pr, av, v_prev);
   if (!group_b) {
@@ -641,15 +639,13 @@ prefill_kernel(PrefillParams p) {
   u32x4 q[G::NSL];
   int bt_next = 0;   // group B: a lane's entry of the next block-table window
   uint32_t bad = 0;
-  // Start of an item: its queries into the wave's LDS area, the V slot of
-  // tile -1 cleared (the first step multiplies a zero P by it, so it must
-  // hold finite values), the copies of K(0), K(1) (group A) and V(0) (group B),
-  // one block per wave each, with the block ids from the descriptor, and
-  // (group B) the loads of block-table window 0, written when the item runs.
+  // Start of an item: its queries into the wave's LDS area, the copies of
+  // K(0), K(1) (group A) and V(0) (group B), one block per wave each, with the
+  // block ids from the descriptor, and (group B) the loads of block-table
+  // window 0, written when the item runs.  (The first step runs no PV, so the
+  // other V slot is not read before V(1) lands in it.)
   auto start_item = [&](const Item<D>& nx, const PrefillItem* d) {
     copy_queries<D>(p, nx.tok0, nx.qw, nx.n, nx.head, lane, lds_addr(io));
-    for (int i = threadIdx.x; i < G::TILEB / 16; i += kWaves * 64)
-      reinterpret_cast<PKV_LDS u32x4*>(sl.v[1])[i] = u32x4{0u, 0u, 0u, 0u};
     const int bid0 = __builtin_amdgcn_readfirstlane(d->bid[wq]);
     const int bid1 = __builtin_amdgcn_readfirstlane(d->bid[4 + wq]);   // block of tile 1
     if (group_b) bt_next = window_entry(nx.bt_row, 0, wave - kWaves / 2, lane, nx.nblk);
@@ -680,7 +676,7 @@ prefill_kernel(PrefillParams p) {
 
     if (group_b) s_bt[0][64 * (wave - kWaves / 2) + lane] = bt_next;   // window 0
     copies_landed<0>();   // the copies of K/V and of the queries
-    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS, the V slot of tile -1 cleared
+    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS
     read_queries<D>(q, io, lane, p.q_sign);
     // asked for only now, so the wait for the copies above does not include it
     if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[queue], 1);
