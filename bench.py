@@ -104,7 +104,12 @@ class Setup:
 
 
 def run_steps(setup, steps, warmup):
-    """Time `steps` steps; returns (ms_per_step, per-kernel mean us)."""
+    """Time `steps` steps; returns (ms_per_step, per-kernel mean us).
+
+    The whole-step time comes from the timed steps alone (nothing but the
+    calls between the two events).  The per-kernel times come from the same
+    number of steps run again afterwards with HIP events recorded around
+    every kernel, which themselves add a few microseconds per step."""
     import torch
 
     pkv = setup.pkv
@@ -119,6 +124,13 @@ def run_steps(setup, steps, warmup):
     torch.cuda.synchronize()
     start, end = mk(), mk()
     start.record()
+    for _ in range(steps):
+        setup.step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+
+    # per-kernel times
     for i in range(steps):
         pkv.paged_attention_set_stage_events(stage_sets[i])
         write_sets[i][0].record()
@@ -126,10 +138,8 @@ def run_steps(setup, steps, warmup):
         write_sets[i][1].record()
         pkv.paged_attention(setup.q, setup.pool, setup.bt, setup.cu, setup.lens, setup.wl.scale,
                             out=setup.out, workspace=setup.ws)
-    end.record()
     torch.cuda.synchronize()
     pkv.paged_attention_set_stage_events(None)
-    ms = start.elapsed_time(end) / steps
     names = ["plan", "decode", "decode_merge", "prefill"]
     us = {n: 1e3 * float(np.mean([s[i].elapsed_time(s[i + 1]) for s in stage_sets]))
           for i, n in enumerate(names)}
@@ -325,7 +335,7 @@ def trace_summary(args):
     with open(path) as fh:
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
     rows = [r for r in rows if "pkv::" in r["Kernel_Name"]]
-    n_dec = args.warmup + args.steps                     # decode_8b steps
+    n_dec = args.warmup + 2 * args.steps                 # decode_8b steps (timed + per-kernel pass)
     phases, seen = {"decode_8b": [], "prefill_8b": []}, 0
     for r in rows:
         if "kv_write" in r["Kernel_Name"]:
