@@ -168,9 +168,12 @@ int paged_attention_set_partition_tokens(int32_t tokens);
  * this thread records events[0] before its first kernel and events[1..4]
  * after the plan, decode, decode-merge and prefill kernels, on the call's
  * stream, so a caller can read each stage's duration with
- * hipEventElapsedTime.  The handles are hipEvent_t values created by the
- * caller, who keeps them alive while calls use them.  count = 0 (or events =
- * NULL) switches it off.  Returns PAGED_EINVAL for other counts. */
+ * hipEventElapsedTime.  A NULL entry leaves that point unrecorded (each
+ * record adds a few microseconds between kernels, so a caller timing one
+ * kernel records only the two events around it).  The handles are
+ * hipEvent_t values created by the caller, who keeps them alive while calls
+ * use them.  count = 0 (or events = NULL) switches it off.  Returns
+ * PAGED_EINVAL for other counts or five NULL entries. */
 int paged_attention_set_stage_events(void* const* events, int32_t count);
 
 const char* paged_last_error(void);

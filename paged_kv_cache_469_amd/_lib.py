@@ -189,12 +189,16 @@ def paged_attention_set_partition_tokens(tokens):
 
 def paged_attention_set_stage_events(events):
     """Record the given 5 torch.cuda.Events around the stages of later
-    paged_attention calls on this thread (None switches it off)."""
+    paged_attention calls on this thread (None switches it off; a None entry
+    leaves that point unrecorded)."""
     if events is None:
         _check(lib().paged_attention_set_stage_events(None, 0))
         return
     handles = []
     for e in events:
+        if e is None:
+            handles.append(None)
+            continue
         if e.cuda_event == 0:          # torch creates the HIP event on first record
             e.record()
         handles.append(e.cuda_event)

@@ -25,7 +25,7 @@ thread_local hipEvent_t g_stage_events[5] = {nullptr, nullptr, nullptr, nullptr,
 thread_local bool g_stage_on = false;
 
 hipError_t stage(int i, hipStream_t stream) {
-  return g_stage_on ? hipEventRecord(g_stage_events[i], stream) : hipSuccess;
+  return g_stage_on && g_stage_events[i] ? hipEventRecord(g_stage_events[i], stream) : hipSuccess;
 }
 std::atomic<int32_t> g_part_tokens{0};
 
@@ -413,10 +413,12 @@ int paged_attention_set_stage_events(void* const* events, int32_t count) {
     return PAGED_OK;
   }
   if (count != 5) return fail(PAGED_EINVAL, "stage events: count must be 0 or 5");
+  bool any = false;
   for (int i = 0; i < 5; ++i) {
-    if (!events[i]) return fail(PAGED_EINVAL, "stage events: null event %d", i);
-    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);   // NULL: that point is not recorded
+    any = any || events[i];
   }
+  if (!any) return fail(PAGED_EINVAL, "stage events: all five are NULL");
   g_stage_on = true;
   return PAGED_OK;
 }
