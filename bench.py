@@ -55,6 +55,8 @@ DESCRIPTIONS = {
                        "64 q / 8 kv heads, head_dim 128; pool ~0.92 of free HBM",
     "spec_verify_8b": "8B-shaped speculative-decoding check: 128 requests x 4 new tokens (3 drafted) "
                       "over cached context U[2048,16384]; 32 q / 8 kv heads, head_dim 128",
+    "spec_verify_70b": "70B-shaped speculative-decoding check: 64 requests x 4 new tokens (3 drafted) "
+                       "over cached context U[4096,16384]; 64 q / 8 kv heads, head_dim 128",
 }
 
 
@@ -474,8 +476,8 @@ def main():
     dom_us = main_res["dom_us"]
     kv_bytes = wl.kv_bytes_unique()
     flops = wl.attention_flops()
-    # segments on the split-context decode path: n * G <= 16 and n <= 8
-    max_dec = min(8, 16 // (wl.num_q_heads // wl.num_kv_heads))
+    # segments on the split-context decode path: n * G <= 32 and n <= 8
+    max_dec = min(8, 32 // (wl.num_q_heads // wl.num_kv_heads))
     decode_segs = np.nonzero((wl.new_tokens >= 1) & (wl.new_tokens <= max_dec))[0]
     prefill_segs = np.nonzero(wl.new_tokens > max_dec)[0]
     dec_bytes = int(wl.seq_lens[decode_segs].astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
@@ -533,7 +535,8 @@ def main():
                           "kernels_us": pr["us"]}
 
     if not args.no_cpu_baseline:
-        if args.workload in ("decode_8b", "long_decode_70b", "cb_step_8b", "spec_verify_8b"):
+        if args.workload in ("decode_8b", "long_decode_70b", "cb_step_8b", "spec_verify_8b",
+                             "spec_verify_70b"):
             import workloads
             base_wl = workloads.make("decode_8b") if args.workload == "decode_8b" else wl
             if args.workload == "decode_8b":

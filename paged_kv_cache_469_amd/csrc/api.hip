@@ -48,9 +48,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kQueryTileMin = 32;   // smallest prefill query tile (heads_per_item = 4)
 
 // Segments with at most this many new tokens take the split-context decode
-// path: their n * G query rows must fit the 16 columns of its products, and
+// path: their n * G query rows must fit its at most two 16-column tiles, and
 // n stays within the few tokens of a speculative-decoding check.
-int32_t max_decode_tokens(int32_t group) { return std::min(8, 16 / std::max(1, group)); }
+int32_t max_decode_tokens(int32_t group) { return std::min(8, 32 / std::max(1, group)); }
 
 // Tokens per decode partition.  Automatic choice: the largest of 1024 .. 64
 // that still gives at least 8192 wave-sized items for the longest allowed

@@ -6,9 +6,10 @@
 // group g (G = Hq/Hkv of them) attend to all L keys of KV head g.  Decode
 // reads every cached K/V byte once per step, so it is bound by HBM bandwidth
 // ("从0开始的vLLM学习": decode is memory-bandwidth bound).  A segment of a few
-// new tokens (n * G <= 16: a speculative-decoding check of n - 1 drafted
+// new tokens (n * G <= 32: a speculative-decoding check of n - 1 drafted
 // tokens, for instance) is the same read: its n * G query rows share the
-// item, and row (token i, head h) sees keys 0 .. L - n + i.
+// item in one or two column tiles of 16, and row (token i, head h) sees keys
+// 0 .. L - n + i.
 //
 // Work split: a work item is (segment, partition of P keys, KV head) and is
 // run by one wavefront; partitions of long contexts run on different waves
@@ -99,55 +100,190 @@ __device__ __forceinline__ void load_kv(KvRegs<D>& r, const BlockRs& b0, const B
   }
 }
 
-template <int D>
-__device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf)[D / 32],
-                                            f32x4 (&o)[D / 16], float& m_run, float& l_run,
-                                            int kb, int kend, bool ok0, bool ok1, int j,
-                                            float scale_log2) {
+// One step of 32 keys for CT column tiles of 16 query rows: the K fragments
+// are multiplied against every tile's queries and each V operand against
+// every tile's P, so the tiles share one read of K and V.
+template <int D, int CT>
+__device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf)[CT][D / 32],
+                                            f32x4 (&o)[CT][D / 16], float (&m_run)[CT],
+                                            float (&l_run)[CT], int kb, const int (&kend)[CT],
+                                            bool ok0, bool ok1, int j, float scale_log2) {
   constexpr int NS = D / 32;
   constexpr int NT = D / 16;
-  f32x4 sc[2];
+  f32x4 sc[CT][2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) sc[b] = mfma16(r.k[b][sl], qf[sl], sc[b]);
-  }
-  float x[8];
-  float cmax = -INFINITY;
+    for (int c = 0; c < CT; ++c) sc[c][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = i >> 2;
-    const bool okb = b ? ok1 : ok0;
-    const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < kend);
-    x[i] = live ? sc[b][i & 3] * scale_log2 : -INFINITY;
-    cmax = fmaxf(cmax, x[i]);
-  }
-  cmax = wave_max_xor(cmax, 16);
-  cmax = wave_max_xor(cmax, 32);
-  const float m_new = fmaxf(m_run, cmax);
-  // all keys so far left out (only for blocks skipped as invalid): keep state
-  const bool none = m_new == -INFINITY;
-  const float alpha = none ? 1.f : exp2f(m_run - m_new);
-  float p[8];
-  float psum = 0.f;
+    for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    p[i] = none ? 0.f : exp2f(x[i] - m_new);
-    psum += p[i];
+      for (int c = 0; c < CT; ++c) sc[c][b] = mfma16(r.k[b][sl], qf[c][sl], sc[c][b]);
   }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  u32x4 pb = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-              pack_bf16(p[6], p[7])};
+  float alpha[CT];
+  u32x4 pb[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    float x[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int b = i >> 2;
+      const bool okb = b ? ok1 : ok0;
+      const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < kend[c]);
+      x[i] = live ? sc[c][b][i & 3] * scale_log2 : -INFINITY;
+      cmax = fmaxf(cmax, x[i]);
+    }
+    cmax = wave_max_xor(cmax, 16);
+    cmax = wave_max_xor(cmax, 32);
+    const float m_new = fmaxf(m_run[c], cmax);
+    // all keys so far left out (blocks skipped as invalid, or keys this row
+    // does not see yet): keep the state
+    const bool none = m_new == -INFINITY;
+    alpha[c] = none ? 1.f : exp2f(m_run[c] - m_new);
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = none ? 0.f : exp2f(x[i] - m_new);
+      psum += p[i];
+    }
+    l_run[c] = l_run[c] * alpha[c] + psum;
+    m_run[c] = m_new;
+    pb[c] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                  pack_bf16(p[6], p[7])};
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    o[t] *= alpha;
     const int w = t >> 1;
     const bool hi = t & 1;
     u32x4 a = {pick_halves(r.v[0][w], r.v[1][w], hi), pick_halves(r.v[2][w], r.v[3][w], hi),
                pick_halves(r.v[4][w], r.v[5][w], hi), pick_halves(r.v[6][w], r.v[7][w], hi)};
-    o[t] = mfma16(a, pb, o[t]);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      o[c][t] *= alpha[c];
+      o[c][t] = mfma16(a, pb[c], o[c][t]);
+    }
+  }
+}
+
+// One work item (segment s, partition part, KV head g) whose n * G query
+// rows fill CT column tiles of 16: row 16c + m is (token ti, head hh) of the
+// segment and sees the partition's keys below kend (causal in the segment).
+template <int D, int CT>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int part, int g, int lane,
+                                            int L, int tok, int n, int row0, int64_t row_bytes,
+                                            int64_t block_bytes) {
+  constexpr int NS = D / 32;
+  constexpr int NT = D / 16;
+  const int m = lane & 15;
+  const int j = lane >> 4;
+  const int key0 = part * p.part_tokens;
+  const int key1 = min(L, key0 + p.part_tokens);
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+
+  int ti[CT], hh[CT], kend[CT];
+  bool live[CT];
+  u32x4 qf[CT][NS];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int row = 16 * c + m;
+    ti[c] = row / p.group;
+    hh[c] = row - ti[c] * p.group;
+    live[c] = ti[c] < n;
+    kend[c] = min(key1, L - n + 1 + ti[c]);
+    const uint16_t* qrow = p.q + (int64_t)(tok + ti[c]) * p.q_stride + (int64_t)(g * p.group + hh[c]) * D + 8 * j;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[c][sl] = live[c] ? *reinterpret_cast<const u32x4*>(qrow + 32 * sl) : z;
+    }
+  }
+  // the partition's block ids, one per lane (P <= 1024 keys = 64 blocks)
+  const int nblk = (key1 - key0 + kBlock - 1) / kBlock;
+  int my_bid = -1;
+  if (lane < nblk) my_bid = p.bt[(int64_t)s * p.width + key0 / kBlock + lane];
+  const bool bad_bid = lane < nblk && (my_bid < 0 || (int64_t)my_bid >= p.num_blocks);
+  if (__any(bad_bid)) {
+    if (lane == 0) atomicOr(&p.hdr->status, 2u);
+  }
+
+  f32x4 o[CT][NT];
+  float m_run[CT], l_run[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+  }
+
+  // block b of the 32 keys starting at kb; its keys count as present
+  // (ok) when the block is inside the pool
+  auto block_at = [&](int kb, int b, bool& ok) -> BlockRs {
+    const int first = kb + kBlock * b;
+    const int nvalid = min(max(key1 - first, 0), kBlock);
+    const int bid = nvalid > 0 ? __builtin_amdgcn_readlane(my_bid, (first - key0) / kBlock) : -1;
+    ok = nvalid > 0 && bid >= 0 && (int64_t)bid < p.num_blocks;
+    return block_rs(p.cache, bid, ok, nvalid, block_bytes, row_bytes, g, D * 2);
+  };
+
+  KvRegs<D> ra, rb;
+  bool ao0, ao1, bo0, bo1;
+  {
+    const BlockRs x0 = block_at(key0, 0, ao0), x1 = block_at(key0, 1, ao1);
+    load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
+  }
+  for (int kb = key0; kb < key1; kb += 64) {
+    const int kn = kb + 32;
+    if (kn < key1) {
+      const BlockRs x0 = block_at(kn, 0, bo0), x1 = block_at(kn, 1, bo1);
+      load_kv<D>(rb, x0, x1, m, j, (uint32_t)row_bytes);
+    }
+    attend_step<D, CT>(ra, qf, o, m_run, l_run, kb, kend, ao0, ao1, j, p.scale_log2);
+    if (kn >= key1) break;
+    const int kn2 = kb + 64;
+    if (kn2 < key1) {
+      const BlockRs x0 = block_at(kn2, 0, ao0), x1 = block_at(kn2, 1, ao1);
+      load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
+    }
+    attend_step<D, CT>(rb, qf, o, m_run, l_run, kn, kend, bo0, bo1, j, p.scale_log2);
+  }
+
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    float l = l_run[c];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!live[c]) continue;
+    const int hq = g * p.group + hh[c];
+    if (nparts == 1) {
+      const float inv = 1.f / l;
+      uint16_t* orow = p.out + ((int64_t)(tok + ti[c]) * p.hq + hq) * D;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        uint32_t wv[NT / 2];
+#pragma unroll
+        for (int t = 0; t < NT; t += 2) wv[t / 2] = pack_bf16(o[c][t][rr] * inv, o[c][t + 1][rr] * inv);
+        uint16_t* dst = orow + NT * (4 * j + rr);
+        if constexpr (NT == 8) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        } else {
+          *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
+        }
+      }
+    } else {
+      const int64_t slot = ((int64_t)(row0 + ti[c]) * p.pmax + part) * p.hq + hq;
+      float* prow = p.part_o + slot * D;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float* dst = prow + NT * (4 * j + rr);
+#pragma unroll
+        for (int t = 0; t < NT; t += 4)
+          *reinterpret_cast<f32x4*>(dst + t) = f32x4{o[c][t][rr], o[c][t + 1][rr], o[c][t + 2][rr], o[c][t + 3][rr]};
+      }
+      if (j == 0) p.part_ml[slot] = make_float2(m_run[c], l);
+    }
   }
 }
 
@@ -155,11 +291,7 @@ __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_kernel(DecodeParams p) {
-  constexpr int NS = D / 32;
-  constexpr int NT = D / 16;
   const int lane = threadIdx.x & 63;
-  const int m = lane & 15;
-  const int j = lane >> 4;
   const int n_items = p.hdr->n_decode * p.hkv;
   if (n_items == 0) return;   // no decode segment in this step: no queue traffic
   const int64_t row_bytes = (int64_t)p.hkv * D * 2;
@@ -179,104 +311,11 @@ decode_kernel(DecodeParams p) {
     const int n = p.cu[s + 1] - tok;
     const int row0 = p.seg_row[s];   // first partial row of the segment
     if (row0 < 0) continue;          // skipped by the plan (and flagged there)
-    const int key0 = part * p.part_tokens;
-    const int key1 = min(L, key0 + p.part_tokens);
-    const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
-
-    // query row m of the item: token ti of the segment, head hh of the group;
-    // it sees the partition's keys below kend (causal within the segment)
-    const int ti = m / p.group;
-    const int hh = m - ti * p.group;
-    const bool head_live = ti < n;
-    const int kend = min(key1, L - n + 1 + ti);
-    u32x4 qf[NS];
-    {
-      const uint16_t* qrow = p.q + (int64_t)(tok + ti) * p.q_stride + (int64_t)(g * p.group + hh) * D + 8 * j;
-#pragma unroll
-      for (int sl = 0; sl < NS; ++sl) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qf[sl] = head_live ? *reinterpret_cast<const u32x4*>(qrow + 32 * sl) : z;
-      }
-    }
-    // the partition's block ids, one per lane (P <= 1024 keys = 64 blocks)
-    const int nblk = (key1 - key0 + kBlock - 1) / kBlock;
-    int my_bid = -1;
-    if (lane < nblk) my_bid = p.bt[(int64_t)s * p.width + key0 / kBlock + lane];
-    const bool bad_bid = lane < nblk && (my_bid < 0 || (int64_t)my_bid >= p.num_blocks);
-    if (__any(bad_bid)) {
-      if (lane == 0) atomicOr(&p.hdr->status, 2u);
-    }
-
-    f32x4 o[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    // block b of the 32 keys starting at kb; its keys count as present
-    // (ok) when the block is inside the pool
-    auto block_at = [&](int kb, int b, bool& ok) -> BlockRs {
-      const int first = kb + kBlock * b;
-      const int nvalid = min(max(key1 - first, 0), kBlock);
-      const int bid = nvalid > 0 ? __builtin_amdgcn_readlane(my_bid, (first - key0) / kBlock) : -1;
-      ok = nvalid > 0 && bid >= 0 && (int64_t)bid < p.num_blocks;
-      return block_rs(p.cache, bid, ok, nvalid, block_bytes, row_bytes, g, D * 2);
-    };
-
-    KvRegs<D> ra, rb;
-    bool ao0, ao1, bo0, bo1;
-    {
-      const BlockRs x0 = block_at(key0, 0, ao0), x1 = block_at(key0, 1, ao1);
-      load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
-    }
-    for (int kb = key0; kb < key1; kb += 64) {
-      const int kn = kb + 32;
-      if (kn < key1) {
-        const BlockRs x0 = block_at(kn, 0, bo0), x1 = block_at(kn, 1, bo1);
-        load_kv<D>(rb, x0, x1, m, j, (uint32_t)row_bytes);
-      }
-      attend_step<D>(ra, qf, o, m_run, l_run, kb, kend, ao0, ao1, j, p.scale_log2);
-      if (kn >= key1) break;
-      const int kn2 = kb + 64;
-      if (kn2 < key1) {
-        const BlockRs x0 = block_at(kn2, 0, ao0), x1 = block_at(kn2, 1, ao1);
-        load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
-      }
-      attend_step<D>(rb, qf, o, m_run, l_run, kn, kend, bo0, bo1, j, p.scale_log2);
-    }
-
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (head_live) {
-      const int hq = g * p.group + hh;
-      if (nparts == 1) {
-        const float inv = 1.f / l_run;
-        uint16_t* orow = p.out + ((int64_t)(tok + ti) * p.hq + hq) * D;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          uint32_t wv[NT / 2];
-#pragma unroll
-          for (int t = 0; t < NT; t += 2) wv[t / 2] = pack_bf16(o[t][rr] * inv, o[t + 1][rr] * inv);
-          uint16_t* dst = orow + NT * (4 * j + rr);
-          if constexpr (NT == 8) {
-            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-          } else {
-            *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
-          }
-        }
-      } else {
-        const int64_t slot = ((int64_t)(row0 + ti) * p.pmax + part) * p.hq + hq;
-        float* prow = p.part_o + slot * D;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          float* dst = prow + NT * (4 * j + rr);
-#pragma unroll
-          for (int t = 0; t < NT; t += 4)
-            *reinterpret_cast<f32x4*>(dst + t) = f32x4{o[t][rr], o[t + 1][rr], o[t + 2][rr], o[t + 3][rr]};
-        }
-        if (j == 0) p.part_ml[slot] = make_float2(m_run, l_run);
-      }
-    }
+    // 16 or 32 query rows (n * G of them live)
+    if (n * p.group <= 16)
+      decode_item<D, 1>(p, s, part, g, lane, L, tok, n, row0, row_bytes, block_bytes);
+    else
+      decode_item<D, 2>(p, s, part, g, lane, L, tok, n, row0, row_bytes, block_bytes);
   }
 }
 

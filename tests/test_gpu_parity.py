@@ -106,8 +106,8 @@ def test_partition_sizes(tokens):
 
 # Segments of a few new tokens over a history (one decode step, or a
 # speculative-decoding check of n - 1 drafted tokens) take the split-context
-# decode path when n * G <= 16 and n <= 8, beside longer segments on the
-# prefill path.  Small partitions give many partials per token, including
+# decode path when n * G <= 32 and n <= 8 (one or two column tiles of 16
+# query rows), beside longer segments on the prefill path.  Small partitions give many partials per token, including
 # last partitions none of whose keys some of the segment's tokens see.
 MULTI = [
     ("g4_d128", dict(hq=32, hkv=8, d=128, segs=[(1, 97), (2, 2), (2, 1025), (3, 67), (4, 4),
@@ -117,6 +117,11 @@ MULTI = [
     ("g2_d128", dict(hq=16, hkv=8, d=128, segs=[(8, 1500), (2, 2), (5, 4100), (9, 9)])),
     ("g8_d64", dict(hq=32, hkv=4, d=64, segs=[(2, 2), (2, 3333), (1, 50), (3, 600)])),
     ("g3_d128", dict(hq=6, hkv=2, d=128, segs=[(5, 800), (4, 4), (2, 2049), (6, 90)])),
+    # two column tiles of 16 rows: n * G in 17 .. 32
+    ("g8_d128_70b", dict(hq=64, hkv=8, d=128, segs=[(4, 5000), (3, 2049), (2, 17), (4, 4),
+                                                    (1, 3000), (5, 900)])),
+    ("g4_d128_long", dict(hq=32, hkv=8, d=128, segs=[(8, 4100), (6, 2500), (7, 33), (8, 8),
+                                                     (9, 300)])),
 ]
 
 

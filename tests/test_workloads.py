@@ -51,6 +51,7 @@ def _check_slots_cover(wl):
                     "chunk": 20, "chunk_history": 48, "decode_first": False}),
     ("long_decode_70b", {"num_requests": 3, "ctx": (100, 300), "num_blocks": 5000}),
     ("spec_verify_8b", {"num_requests": 5, "ctx": (30, 90)}),
+    ("spec_verify_70b", {"num_requests": 4, "ctx": (30, 90)}),
 ])
 def test_structure(name, kw):
     wl = workloads.make(name, **kw)

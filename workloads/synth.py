@@ -320,6 +320,16 @@ def spec_verify_8b(num_requests=128, drafts=3, ctx=(2048, 16384), **kw):
     return build("spec_verify_8b", 6, 32, 8, 128, [(n, int(x) + n) for x in c], **kw)
 
 
+def spec_verify_70b(num_requests=64, drafts=3, ctx=(4096, 16384), **kw):
+    """70B-shaped speculative-decoding check (64 q heads, 8 KV heads, head_dim
+    128): each request feeds its last accepted token and ``drafts`` drafted
+    ones over a cached context uniform in ``ctx``; n * G = 32 query rows per
+    KV head."""
+    c = _rng(7, 0).integers(ctx[0], ctx[1] + 1, size=num_requests)
+    n = drafts + 1
+    return build("spec_verify_70b", 7, 64, 8, 128, [(n, int(x) + n) for x in c], **kw)
+
+
 NAMED = {
     "tiny_mixed": tiny_mixed,
     "decode_8b": decode_8b,
@@ -327,6 +337,7 @@ NAMED = {
     "cb_step_8b": cb_step_8b,
     "long_decode_70b": long_decode_70b,
     "spec_verify_8b": spec_verify_8b,
+    "spec_verify_70b": spec_verify_70b,
 }
 
 
