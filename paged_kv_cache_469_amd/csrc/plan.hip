@@ -114,6 +114,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   uint32_t status = 0;
   SegInfo first{0, 0, 0, false};   // the thread's segment of the first 1024, kept for the later passes
   int first_ofull = 0;              // and the place of its first full decode partition
+  int first_tot_f = 0;              // and the first chunk's full decode partitions in all
   int full_base = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
@@ -136,7 +137,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     block_exclusive_scan(nd, scratch, &tot_d);
     const int nfull = nd > 0 ? si.L / p.part_tokens : 0;
     const int ofull = full_base + block_exclusive_scan(nfull, scratch, &tot_f);
-    if (base == 0) first_ofull = ofull;
+    if (base == 0) {
+      first_ofull = ofull;
+      first_tot_f = tot_f;
+    }
     full_base += tot_f;
     // one scan counts the prefill items (low 20 bits: fewer than 2^20 per
     // call) and places the prefill segments in the list (bits 20 and up)
@@ -201,7 +205,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     const bool dec = si.ok && si.n >= 1 && si.n <= p.max_decode_n;
     const int full = dec ? si.L / p.part_tokens : 0;
     int at = first_ofull;
-    if (base > 0) {   // more than 1024 segments: place the full partitions again
+    if (base == 0) {
+      full_base = first_tot_f;
+    } else {   // more than 1024 segments: place the full partitions again
       int tot_f;
       at = full_base + block_exclusive_scan(full, scratch, &tot_f);
       full_base += tot_f;

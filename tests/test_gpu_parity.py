@@ -157,6 +157,34 @@ def test_multi_token_decode_sharpened():
     check_close(out, ref, "multi-token sharpened")
 
 
+def test_more_than_1024_segments():
+    # the plan kernel walks segments in chunks of 1024 threads: decode items,
+    # partial rows and prefill items of later chunks take its second path
+    rng = np.random.default_rng([469, 52, 0])
+    segs = []
+    for i in range(1100):
+        if i in (3, 700, 1030, 1090):
+            n = int(rng.integers(65, 200))
+            segs.append((n, n + int(rng.integers(0, 100))))
+        elif i % 97 == 5:
+            segs.append((int(rng.integers(2, 5)), int(rng.integers(40, 300))))
+        else:
+            segs.append((1, int(rng.integers(1, 120))))
+    wl = _custom(32, 8, 128, segs, cfg=53, num_blocks=None)
+    log(f"case 1100 segments: T={wl.num_tokens} NB={wl.num_blocks}")
+    pkv.paged_attention_set_partition_tokens(64)   # several partitions per longer decode
+    try:
+        st = DeviceStep(wl, host_pool=True)
+        out = down_u16(st.attend())
+    finally:
+        pkv.paged_attention_set_partition_tokens(0)
+    assert np.array_equal(down_u16(st.pool), st.host)
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens,
+                       wl.scale)
+    check_close(out, ref, "1100 segments")
+    assert st.status() == 0
+
+
 def test_permutation_invariance_and_determinism():
     kw = dict(num_decodes=10, ctx=(1024, 2500), shared=3, prefix=1024, chunk=130, chunk_history=300)
     a = workloads.make("cb_step_8b", **kw)
