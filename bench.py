@@ -355,25 +355,35 @@ def pmc_summary(args):
 
 
 def trace_summary(args):
-    """Per-kernel durations from a rocprofv3 --kernel-trace CSV of the default
-    bench command, split into its two phases (decode_8b, then prefill_8b) by
-    counting the KV-write dispatches that open every step."""
+    """Per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench
+    command.  For the default command (decode_8b) the trace is split into its
+    two phases (decode_8b, then prefill_8b) by counting the KV-write
+    dispatches that open every step; for another --workload it is one phase."""
     path = glob.glob(os.path.join(args.trace, "*kernel_trace.csv"))[0]
     with open(path) as fh:
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
     rows = [r for r in rows if "pkv::" in r["Kernel_Name"]]
-    n_dec = args.warmup + 3 * args.steps                 # decode_8b steps (timed + two event passes)
-    phases, seen = {"decode_8b": [], "prefill_8b": []}, 0
-    for r in rows:
-        if "kv_write" in r["Kernel_Name"]:
-            seen += 1
-        phases["decode_8b" if seen <= n_dec else "prefill_8b"].append(r)
-    out = [f"# Kernel trace: default bench (decode_8b headline, prefill_8b line item)", "",
+    default = args.workload == "decode_8b"
+    wl_flag = "" if default else f" --workload {args.workload}"
+    if default:
+        n_dec = args.warmup + 3 * args.steps             # decode_8b steps (timed + two event passes)
+        phases, seen = {"decode_8b": [], "prefill_8b": []}, 0
+        for r in rows:
+            if "kv_write" in r["Kernel_Name"]:
+                seen += 1
+            phases["decode_8b" if seen <= n_dec else "prefill_8b"].append(r)
+        title = "default bench (decode_8b headline, prefill_8b line item)"
+    else:
+        phases = {args.workload: rows}
+        title = f"{args.workload}: {DESCRIPTIONS[args.workload]}"
+    out = [f"# Kernel trace: {title}", "",
            "Command (from the repository root, on one MI355X):", "",
-           f"    rocprofv3 --kernel-trace --stats -f csv -d <T> -o kt -- python bench.py "
+           f"    rocprofv3 --kernel-trace --stats -f csv -d <T> -o kt -- python bench.py{wl_flag} "
            f"--steps {args.steps} --warmup {args.warmup} --no-cpu-baseline",
-           f"    python bench.py --trace-summary --trace <T> --steps {args.steps} --warmup {args.warmup}",
-           "", "Durations in microseconds (end - start of each dispatch).", ""]
+           f"    python bench.py --trace-summary --trace <T>{wl_flag} --steps {args.steps} --warmup {args.warmup}",
+           "", "Durations in microseconds (end - start of each dispatch): per step one warm-up, then "
+           "three passes of the steps (timed; events around the roofline kernel; events around "
+           "every kernel).", ""]
     for ph, rs in phases.items():
         by = {}
         for r in rs:
