@@ -32,8 +32,10 @@ list (removal from the middle is ``list.remove``), so operations are O(n),
 not O(1) -- this model is for checking, not for speed.
 
 Parity status: pinned by ``tests/test_oracle_block_manager.py`` (the pages'
-prefix-caching scenario worked by hand, invariants under random operation
-sequences, and a brute-force longest-prefix check).
+prefix-caching scenario and smaller cases worked by hand, invariants under
+random operation sequences, and a brute-force longest-prefix check);
+``tests/test_oracle_bm_mutations.py`` checks that planted mistakes in a copy
+of this model fail those pins.
 """
 
 BLOCK = 16

@@ -170,3 +170,40 @@ def test_step_metadata_drives_paged_attention(have_lib):
             assert np.array_equal(out[cu[s]:cu[s + 1]], ref), f"request {r}"
     assert bm.ref_count(bm.block_table(2)[0]) == 4     # the system prompt's first block is shared
     bm.close()
+
+
+SCENARIOS = {
+    # hits that sit in the free queue are not free blocks
+    "hits_not_free": (3, [("add", 1, list(range(33))), ("alloc", 1, 33), ("free", 1, None),
+                          ("add", 2, list(range(32)) + list(range(100, 117))), ("alloc", 2, 17),
+                          ("add", 3, list(range(32)) + [5]), ("alloc", 3, 1)]),
+    # the same prompt chunked side by side: one match, one registration per key
+    "concurrent_prompts": (8, [("add", 1, list(range(40))), ("add", 2, list(range(40))),
+                               ("alloc", 1, 10), ("alloc", 2, 16), ("alloc", 1, 30),
+                               ("alloc", 2, 24), ("add", 3, list(range(40))), ("alloc", 3, 8),
+                               ("free", 1, None), ("free", 2, None), ("alloc", 3, 0)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCENARIOS))
+def test_matches_model_on_scenarios(have_lib, name):
+    nb, ops = SCENARIOS[name]
+    cpp, model = pkv.BlockManager(nb), BlockManagerModel(nb)
+    live = []
+    for op, req, arg in ops:
+        if op == "add":
+            cpp.add_request(req, arg)
+            model.add_request(req, arg)
+            assert cpp.num_cached_tokens(req) == model.num_cached_tokens(req)
+            live.append(req)
+        elif op == "alloc":
+            a, b = cpp.allocate_slots(req, arg), model.allocate_slots(req, arg)
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert a.tolist() == b
+        else:
+            cpp.free_request(req)
+            model.free_request(req)
+            live.remove(req)
+        _same_state(cpp, model, live)
+    cpp.close()

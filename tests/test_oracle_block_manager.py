@@ -161,3 +161,70 @@ def test_invariants_under_random_operations(seed):
             req = live.pop(int(rng.integers(0, len(live))))
             m.free_request(req)
         _check_invariants(m)
+
+
+def test_step_metadata_by_hand():
+    # one table per request, -1 padded; the new tokens are each request's
+    # last n positions, packed in the order given (section 1.5)
+    m = BlockManagerModel(6, prefix_caching=False)
+    m.add_request(1, list(range(20)))
+    m.add_request(2, list(range(5)))
+    assert m.allocate_slots(1, 20) == list(range(20))          # blocks 0, 1
+    assert m.allocate_slots(2, 3) == _slots([(2, 0), (2, 1), (2, 2)])   # a chunk of 3
+    tables, cu, lens, slots = m.step_metadata([1, 2], [20, 3], 3)
+    assert tables == [[0, 1, -1], [2, -1, -1]]
+    assert cu == [0, 20, 23] and lens == [20, 3]
+    assert slots == list(range(20)) + _slots([(2, 0), (2, 1), (2, 2)])
+    m.append_tokens(1, [7])
+    assert m.allocate_slots(1, 1) == _slots([(1, 4)])          # position 20
+    assert m.allocate_slots(2, 2) == _slots([(2, 3), (2, 4)])
+    tables, cu, lens, slots = m.step_metadata([2, 1], [2, 1], 3)
+    assert tables == [[2, -1, -1], [0, 1, -1]]
+    assert cu == [0, 2, 3] and lens == [5, 21]
+    assert slots == _slots([(2, 3), (2, 4), (1, 4)])
+    with pytest.raises(ValueError):
+        m.step_metadata([2], [6], 3)                            # more new tokens than L
+    with pytest.raises(ValueError):
+        m.step_metadata([1], [1], 1)                            # table wider than the row
+
+
+def test_cached_hits_in_the_free_queue_are_not_free():
+    # a released, still-cached block that a request hits leaves the free
+    # queue, so it cannot also be handed out as a new block (section 1.4:
+    # the scheduler must preempt when blocks run out)
+    m = BlockManagerModel(3)
+    prompt = list(range(33))
+    m.add_request(1, prompt)
+    m.allocate_slots(1, 33)                        # blocks 0, 1 cached, 2 partial
+    m.free_request(1)
+    assert m.free == [2, 1, 0] and m.num_cached_blocks() == 2
+    m.add_request(2, prompt[:32] + list(range(100, 117)))   # 49 tokens: 4 blocks
+    assert m.num_cached_tokens(2) == 32
+    assert m.allocate_slots(2, 17) is None         # 2 hits + 2 new > 3 blocks
+    assert m.free == [2, 1, 0] and m.block_table(2) == []
+    m.add_request(3, prompt[:32] + [5])
+    assert m.allocate_slots(3, 1) == [2 * BLOCK]   # 2 hits + 1 new fits exactly
+    assert m.free == []
+
+
+def test_concurrent_prompts_match_once_and_register_once():
+    # two requests with the same prompt, chunked side by side: the second
+    # matched nothing at its first allocation and matches nothing later, and
+    # a block filled with content already registered to another block stays
+    # unregistered
+    m = BlockManagerModel(8)
+    prompt = list(range(40))
+    m.add_request(1, prompt)
+    m.add_request(2, prompt)
+    assert m.allocate_slots(1, 10) == list(range(10))                  # block 0, partial
+    assert m.allocate_slots(2, 16) == _slots([(1, r) for r in range(16)])
+    assert m.key[1] is not None                                         # block 1 registered first
+    assert m.allocate_slots(1, 30) == list(range(10, 16)) + list(range(32, 56))
+    assert m.block_table(1) == [0, 2, 3]
+    assert m.key[0] is None and m.num_cached_blocks() == 2              # same content as block 1
+    assert m.num_cached_tokens(2) == 16                                 # no late matching
+    assert m.allocate_slots(2, 24) == _slots([(4, r) for r in range(16)] + [(5, r) for r in range(8)])
+    assert m.block_table(2) == [1, 4, 5]
+    assert m.key[4] is None and m.num_cached_blocks() == 2
+    m.add_request(3, prompt)
+    assert m.num_cached_tokens(3) == 32 and m._match(m.reqs[3]) == [1, 2]
