@@ -438,6 +438,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=160, help="decode requests the oracle runs")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--group-members", type=int, default=0,
+                    help="most members of a shared-prefix group (0: automatic, 1: no groups)")
     ap.add_argument("--pmc-summary", action="store_true",
                     help="summarise four rocprofv3 counter runs (see --fetch .. --calib-write)")
     ap.add_argument("--trace-summary", action="store_true",
@@ -475,6 +477,8 @@ def main():
     pkv.lib()
     if args.partition_tokens:
         pkv.paged_attention_set_partition_tokens(args.partition_tokens)
+    if args.group_members:
+        pkv.paged_attention_set_group_members(args.group_members)
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     paged_attention,
     paged_attention_device_status,
     paged_attention_set_partition_tokens,
+    paged_attention_set_group_members,
     paged_attention_set_stage_events,
     paged_attention_workspace_size,
     paged_decode_advance,

@@ -29,6 +29,7 @@ _SIGS = {
                                 _c_i32, _c_p]),
     "paged_attention_device_status": (_c_i32, [_c_p, ctypes.POINTER(ctypes.c_uint32), _c_p]),
     "paged_attention_set_partition_tokens": (_c_i32, [_c_i32]),
+    "paged_attention_set_group_members": (_c_i32, [_c_i32]),
     "paged_attention_set_stage_events": (_c_i32, [ctypes.POINTER(_c_p), _c_i32]),
     "paged_decode_advance": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i64, _c_p]),
     "paged_last_error": (ctypes.c_char_p, []),
@@ -185,6 +186,10 @@ def paged_attention_device_status(workspace, stream=None):
 
 def paged_attention_set_partition_tokens(tokens):
     _check(lib().paged_attention_set_partition_tokens(int(tokens)))
+
+
+def paged_attention_set_group_members(members):
+    _check(lib().paged_attention_set_group_members(int(members)))
 
 
 def paged_attention_set_stage_events(events):

@@ -28,6 +28,7 @@ hipError_t stage(int i, hipStream_t stream) {
   return g_stage_on && g_stage_events[i] ? hipEventRecord(g_stage_events[i], stream) : hipSuccess;
 }
 std::atomic<int32_t> g_part_tokens{0};
+std::atomic<int32_t> g_group_members{0};   // 0: automatic, 1: no shared-prefix groups
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -52,6 +53,14 @@ constexpr int kQueryTileMin = 32;   // smallest prefill query tile (heads_per_it
 // n stays within the few tokens of a speculative-decoding check.
 int32_t max_decode_tokens(int32_t group) { return std::min(8, 32 / std::max(1, group)); }
 
+// Most members of a shared-prefix group: the group's query rows (members * G)
+// fill at most two 16-row column tiles of the decode kernel.
+int32_t group_members(int32_t group) {
+  const int32_t cap = std::min(8, 32 / std::max(1, group));
+  const int32_t forced = g_group_members.load();
+  return forced > 0 ? std::min(cap, forced) : cap;
+}
+
 // Tokens per decode partition.  Automatic choice: the largest of 1024 .. 64
 // that still gives at least 8192 wave-sized items for the longest allowed
 // context (the items then outnumber the chip's resident waves several times,
@@ -74,7 +83,9 @@ struct Layout {
   int64_t decode_cap = 0;
   int64_t prefill_cap = 0;
   int64_t rows_cap = 0;   // partial rows: one per new token of a decode segment
-  size_t decode_items = 0, prefill_items = 0, seg_row = 0, part_ml = 0, part_o = 0, total = 0;
+  int64_t group_cap = 0;  // shared-prefix group items: each replaces two or more decode items
+  size_t decode_items = 0, prefill_items = 0, seg_row = 0, group_items = 0, part_ml = 0,
+         part_o = 0, total = 0;
 };
 
 Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int32_t head_dim,
@@ -95,6 +106,9 @@ Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int
   off = align256(off + (size_t)l.prefill_cap * sizeof(pkv::PrefillItem));
   l.seg_row = off;
   off = align256(off + (size_t)num_seqs * sizeof(int32_t));
+  l.group_cap = l.decode_cap / 2 + 1;
+  l.group_items = off;
+  off = align256(off + (size_t)l.group_cap * sizeof(int4));
   l.part_ml = off;
   off = align256(off + (size_t)l.rows_cap * l.pmax * hq * sizeof(float2));
   l.part_o = off;
@@ -255,6 +269,9 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   pp.seg_row = reinterpret_cast<int32_t*>(ws + l.seg_row);
   pp.max_decode_n = max_decode_tokens(group);
   pp.rows_cap = (int32_t)l.rows_cap;
+  pp.group_items = reinterpret_cast<int4*>(ws + l.group_items);
+  pp.group_cap = (int32_t)l.group_cap;
+  pp.group_max = group_members(group);
   e = stage(0, stream);
   if (e == hipSuccess) e = launch_plan(pp, stream);
   if (e == hipSuccess) e = stage(1, stream);
@@ -272,6 +289,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   dp.part_ml = reinterpret_cast<float2*>(ws + l.part_ml);
   dp.hdr = hdr;
   dp.items = pp.decode_items;
+  dp.groups = pp.group_items;
   dp.seg_row = pp.seg_row;
   dp.q_stride = q_token_stride;
   dp.num_blocks = num_blocks;
@@ -404,6 +422,13 @@ int paged_attention_set_partition_tokens(int32_t tokens) {
   if (tokens != 0 && (tokens < 32 || tokens > 1024 || tokens % 32))
     return fail(PAGED_EINVAL, "partition tokens must be 0 or a multiple of 32 in [32, 1024]");
   g_part_tokens.store(tokens);
+  return PAGED_OK;
+}
+
+int paged_attention_set_group_members(int32_t members) {
+  if (members < 0 || members > 8)
+    return fail(PAGED_EINVAL, "group members must be in [0, 8] (0: automatic, 1: off)");
+  g_group_members.store(members);
   return PAGED_OK;
 }
 

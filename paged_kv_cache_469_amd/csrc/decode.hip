@@ -167,42 +167,43 @@ __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf
   }
 }
 
-// One work item (segment s, partition part, KV head g) whose n * G query
-// rows fill CT column tiles of 16: row 16c + m is (token ti, head hh) of the
-// segment and sees the partition's keys below kend (causal in the segment).
+// Query rows of one work item: CT column tiles of 16 rows; row 16c + m reads
+// token qtok[c] of the packed batch, query head hq[c], sees the partition's
+// keys below kend[c], and leaves its result in partial row prow[c] (or, when
+// the item is the whole context, in output row qtok[c]).
+template <int CT>
+struct RowMap {
+  int qtok[CT], hq[CT], kend[CT], prow[CT];
+  bool live[CT];
+};
+
+// One work item: the keys key0 .. key1 - 1 of the block table row `bt_row`
+// for KV head g, attended by the query rows of `rm`.
 template <int D, int CT>
-__device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int part, int g, int lane,
-                                            int L, int tok, int n, int row0, int64_t row_bytes,
+__device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t* bt_row, int key0,
+                                            int key1, int part, bool direct, int g, int lane,
+                                            const RowMap<CT>& rm, int64_t row_bytes,
                                             int64_t block_bytes) {
   constexpr int NS = D / 32;
   constexpr int NT = D / 16;
   const int m = lane & 15;
   const int j = lane >> 4;
-  const int key0 = part * p.part_tokens;
-  const int key1 = min(L, key0 + p.part_tokens);
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
-
-  int ti[CT], hh[CT], kend[CT];
-  bool live[CT];
+  int kend[CT];
   u32x4 qf[CT][NS];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    const int row = 16 * c + m;
-    ti[c] = row / p.group;
-    hh[c] = row - ti[c] * p.group;
-    live[c] = ti[c] < n;
-    kend[c] = min(key1, L - n + 1 + ti[c]);
-    const uint16_t* qrow = p.q + (int64_t)(tok + ti[c]) * p.q_stride + (int64_t)(g * p.group + hh[c]) * D + 8 * j;
+    kend[c] = rm.kend[c];
+    const uint16_t* qrow = p.q + (int64_t)rm.qtok[c] * p.q_stride + (int64_t)rm.hq[c] * D + 8 * j;
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      qf[c][sl] = live[c] ? *reinterpret_cast<const u32x4*>(qrow + 32 * sl) : z;
+      qf[c][sl] = rm.live[c] ? *reinterpret_cast<const u32x4*>(qrow + 32 * sl) : z;
     }
   }
   // the partition's block ids, one per lane (P <= 1024 keys = 64 blocks)
   const int nblk = (key1 - key0 + kBlock - 1) / kBlock;
   int my_bid = -1;
-  if (lane < nblk) my_bid = p.bt[(int64_t)s * p.width + key0 / kBlock + lane];
+  if (lane < nblk) my_bid = bt_row[key0 / kBlock + lane];
   const bool bad_bid = lane < nblk && (my_bid < 0 || (int64_t)my_bid >= p.num_blocks);
   if (__any(bad_bid)) {
     if (lane == 0) atomicOr(&p.hdr->status, 2u);
@@ -255,11 +256,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int pa
     float l = l_run[c];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (!live[c]) continue;
-    const int hq = g * p.group + hh[c];
-    if (nparts == 1) {
+    if (!rm.live[c]) continue;
+    const int hq = rm.hq[c];
+    if (direct) {
       const float inv = 1.f / l;
-      uint16_t* orow = p.out + ((int64_t)(tok + ti[c]) * p.hq + hq) * D;
+      uint16_t* orow = p.out + ((int64_t)rm.qtok[c] * p.hq + hq) * D;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         uint32_t wv[NT / 2];
@@ -273,7 +274,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int pa
         }
       }
     } else {
-      const int64_t slot = ((int64_t)(row0 + ti[c]) * p.pmax + part) * p.hq + hq;
+      const int64_t slot = ((int64_t)rm.prow[c] * p.pmax + part) * p.hq + hq;
       float* prow = p.part_o + slot * D;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
@@ -287,12 +288,92 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int pa
   }
 }
 
+// Work item (segment s, partition part, KV head g) of a decode segment of n
+// new tokens: row 16c + m is (token ti, head hh) of the segment and sees the
+// partition's keys up to its own position (causal in the segment).
+template <int D, int CT>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int part, int g, int lane,
+                                            int L, int tok, int n, int row0, int64_t row_bytes,
+                                            int64_t block_bytes) {
+  const int key0 = part * p.part_tokens;
+  const int key1 = min(L, key0 + p.part_tokens);
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  RowMap<CT> rm;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int row = 16 * c + (lane & 15);
+    const int ti = row / p.group;
+    rm.live[c] = ti < n;
+    rm.kend[c] = min(key1, L - n + 1 + ti);
+    rm.qtok[c] = tok + ti;
+    rm.hq[c] = g * p.group + (row - ti * p.group);
+    rm.prow[c] = row0 + ti;
+  }
+  decode_rows<D, CT>(p, p.bt + (int64_t)s * p.width, key0, key1, part, nparts == 1, g, lane, rm,
+                     row_bytes, block_bytes);
+}
+
+// Group item (segments s0 .. s0 + nmem - 1, partition part, KV head g) of
+// single-token decode segments that the plan found to share this full
+// partition (by its first block id): each member's block ids of the
+// partition are compared with the first member's, and the keys are read once
+// for all members that match.  Row 16c + m is (member mi, head hh) and sees
+// all P keys (each member's token comes after them); results go to each
+// member's own partial row.  A member whose ids differ is computed on its own
+// afterwards, from its own table.
+template <int D, int CT>
+__device__ __forceinline__ void group_item(const DecodeParams& p, int s0, int part, int nmem, int g,
+                                           int lane, int64_t row_bytes, int64_t block_bytes) {
+  const int key0 = part * p.part_tokens;
+  const int key1 = key0 + p.part_tokens;
+  const int npb = p.part_tokens / kBlock;   // <= 64: one id per lane
+  const int32_t* first = p.bt + (int64_t)s0 * p.width + key0 / kBlock;
+  int ids[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    ids[i] = lane < npb ? first[(int64_t)min(i, nmem - 1) * p.width + lane] : 0;
+  uint32_t differ = 0;
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+    if (i < nmem && __any(ids[i] != ids[0])) differ |= 1u << i;
+  RowMap<CT> rm;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int row = 16 * c + (lane & 15);
+    const int mi = row / p.group;
+    const int sm = s0 + min(mi, nmem - 1);
+    const int r0 = p.seg_row[sm];
+    rm.live[c] = mi < nmem && r0 >= 0 && !((differ >> mi) & 1u);
+    rm.kend[c] = key1;
+    rm.qtok[c] = p.cu[sm];
+    rm.hq[c] = g * p.group + (row - mi * p.group);
+    rm.prow[c] = r0;
+  }
+  decode_rows<D, CT>(p, p.bt + (int64_t)s0 * p.width, key0, key1, part, false, g, lane, rm,
+                     row_bytes, block_bytes);
+  while (differ) {
+    const int mi = __builtin_ctz(differ);
+    differ &= differ - 1;
+    const int sm = s0 + mi;
+    const int hh = lane & 15;
+    RowMap<1> one;
+    one.live[0] = hh < p.group && p.seg_row[sm] >= 0;
+    one.kend[0] = key1;
+    one.qtok[0] = p.cu[sm];
+    one.hq[0] = g * p.group + min(hh, p.group - 1);
+    one.prow[0] = p.seg_row[sm];
+    decode_rows<D, 1>(p, p.bt + (int64_t)sm * p.width, key0, key1, part, false, g, lane, one,
+                      row_bytes, block_bytes);
+  }
+}
+
 // One wave per SIMD: forcing two (256 registers each) measured slower.
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
-  const int n_items = p.hdr->n_decode * p.hkv;
+  const int n_grp = p.hdr->n_group * p.hkv;   // group items come first: every one is a full partition
+  const int n_items = n_grp + p.hdr->n_decode * p.hkv;
   if (n_items == 0) return;   // no decode segment in this step: no queue traffic
   const int64_t row_bytes = (int64_t)p.hkv * D * 2;
   const int64_t block_bytes = 2 * kBlock * row_bytes;
@@ -302,6 +383,16 @@ decode_kernel(DecodeParams p) {
     if (lane == 0) it = atomicAdd(&p.hdr->decode_next, 1);
     it = wave_uniform(__shfl(it, 0));
     if (it >= n_items) break;
+    if (it < n_grp) {
+      const int4 gi = p.groups[it / p.hkv];
+      const int g = it % p.hkv;
+      if (gi.z * p.group <= 16)
+        group_item<D, 1>(p, gi.x, gi.y, gi.z, g, lane, row_bytes, block_bytes);
+      else
+        group_item<D, 2>(p, gi.x, gi.y, gi.z, g, lane, row_bytes, block_bytes);
+      continue;
+    }
+    it -= n_grp;
     const int2 item = p.items[it / p.hkv];
     const int g = it % p.hkv;
     const int s = item.x;

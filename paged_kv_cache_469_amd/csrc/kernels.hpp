@@ -27,6 +27,7 @@ struct PlanParams {
   int2* decode_items;
   PrefillItem* prefill_items;
   int32_t* seg_row;      // per segment: first partial row of a decode segment, else -1
+  int4* group_items;     // shared-prefix groups: (first segment, partition, members, 0)
   int32_t num_seqs;
   int32_t num_tokens;
   int32_t width;         // block-table row length
@@ -37,6 +38,8 @@ struct PlanParams {
   int32_t prefill_cap;   // capacity of prefill_items
   int32_t max_decode_n;  // segments with 1 <= n <= this take the decode path
   int32_t rows_cap;      // partial rows (one per new token of a decode segment)
+  int32_t group_cap;     // capacity of group_items
+  int32_t group_max;     // most members of a group (0 or 1: no grouping)
 };
 
 struct DecodeParams {
@@ -51,6 +54,7 @@ struct DecodeParams {
   const int32_t* seg_row;  // per segment: its first partial row (token 0), -1 if not decode
   WsHeader* hdr;
   const int2* items;       // (segment, partition)
+  const int4* groups;      // (first segment, partition, members, 0), taken before items
   int64_t q_stride;
   int64_t num_blocks;
   int32_t width;           // block table row length

@@ -7,9 +7,10 @@
 // host never reads metadata and the whole call can be captured in a graph:
 //   1 <= n <= N_dec -> decode: ceil(L / P) items (segment, partition); the
 //             segment's n tokens get n consecutive rows of partial results
-//             (seg_row[s] is the first), n * G <= 16 query rows per KV head
+//             (seg_row[s] is the first), n * G <= 32 query rows per KV head
 //             (one decode step, or a few tokens of a speculative-decoding
-//             check, over a long history)
+//             check, over a long history); leading partitions shared with
+//             neighbouring segments go to group items instead (pass 0)
 //   n >  N_dec -> prefill: ceil(n / QT) items (segment, query tile), each
 //             with the segment bounds and its first eight block ids
 //   n == 0 -> nothing
@@ -57,6 +58,32 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
   return res;
 }
 
+// Inclusive maximum over the 1024 threads of the block.
+__device__ int block_inclusive_max(int v, int* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x = max(x, y);
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = INT_MIN;
+    for (int w = 0; w < 16; ++w) {
+      const int t = scratch[w];
+      scratch[w] = run;
+      run = max(run, t);
+    }
+  }
+  __syncthreads();
+  const int res = max(scratch[wave], x);
+  __syncthreads();
+  return res;
+}
+
 struct SegInfo {
   int n, L, c0;
   bool ok;
@@ -98,6 +125,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   // wave per segment spreads its query tiles over the lanes
   __shared__ int pl_seg[1024], pl_n[1024], pl_len[1024], pl_c0[1024];
   __shared__ int pl_count;
+  // shared-prefix grouping of a batch of at most 1024 segments
+  __shared__ int g_fb[1024], g_len[1024], g_link[1024], g_cand[1024], g_size[1024], g_cnt[1024];
   const bool one_chunk = p.num_seqs <= 1024;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -105,6 +134,93 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   if (threadIdx.x < kDecodeBuckets) dhist[threadIdx.x] = 0;
   if (threadIdx.x < 16) p.hdr->zeros[threadIdx.x] = 0u;
   __syncthreads();
+
+  // pass 0: shared-prefix groups.  Consecutive single-token decode segments
+  // of more than one partition whose leading full partitions start with the
+  // same block ids (a cached prefix the block manager shares, "vLLM 学习笔记
+  // 01", section 2.2) form runs; each run is cut into groups of at most
+  // group_max members, and a group reads each partition that all its
+  // members share once, for all of them (one group item per partition).
+  // Those partitions leave the members' own item lists.  A first table
+  // entry equal to the previous segment's makes a candidate.
+  SegInfo si0{0, 0, 0, false};
+  int cov = 0;       // leading partitions of the thread's segment that group items cover
+  int n_group = 0;
+  if (one_chunk) si0 = seg_info(p, threadIdx.x);
+  if (one_chunk && p.group_max >= 2) {
+    const int s = threadIdx.x;
+    const bool elig = si0.ok && si0.n == 1 && si0.L > p.part_tokens;
+    g_fb[s] = elig ? p.bt[(int64_t)s * p.width] : 0;
+    g_len[s] = elig ? si0.L : 0;   // 0: not eligible
+    g_link[s] = 0;
+    __syncthreads();
+    const bool cand = elig && s > 0 && g_len[s - 1] > 0 && g_fb[s] == g_fb[s - 1];
+    int ncand;
+    const int ci = block_exclusive_scan(cand ? 1 : 0, scratch, &ncand);
+    if (cand) g_cand[ci] = s;
+    __syncthreads();
+    if (ncand > 0) {
+      // link of each candidate: how many leading full partitions it has whose
+      // first block ids equal the previous segment's.  Only the first id of
+      // a partition is compared here (one pair of loads per partition, all
+      // in one trip to memory); the decode kernel compares a grouped
+      // partition's ids whole and computes a member that differs on its own.
+      // Rounds of 8 partitions: a unit is (candidate, partition); g_size
+      // holds a candidate's first differing partition, g_cnt marks finished
+      // candidates.
+      constexpr int kRound = 8;
+      const int npb = p.part_tokens / kBlock;   // block ids per partition
+      if ((int)threadIdx.x < ncand) g_cnt[threadIdx.x] = 0;
+      for (int c0 = 0;; c0 += kRound) {
+        if ((int)threadIdx.x < ncand) g_size[threadIdx.x] = INT_MAX;
+        __syncthreads();
+        for (int u = threadIdx.x; u < ncand * kRound; u += 1024) {
+          const int k = u / kRound;
+          if (g_cnt[k]) continue;
+          const int sc = g_cand[k];
+          const int c = c0 + u % kRound;
+          // a partition counts when it is full in both segments
+          bool differ = c >= min(g_len[sc], g_len[sc - 1]) / p.part_tokens;
+          if (!differ) {
+            const int32_t* a = p.bt + (int64_t)sc * p.width + c * npb;
+            differ = a[0] != a[-(int64_t)p.width];
+          }
+          if (differ) atomicMin(&g_size[k], c);
+        }
+        __syncthreads();
+        int more = 0;
+        if ((int)threadIdx.x < ncand && !g_cnt[threadIdx.x]) {
+          const int f = g_size[threadIdx.x];
+          g_link[g_cand[threadIdx.x]] = min(f, c0 + kRound);
+          if (f == INT_MAX)
+            more = 1;
+          else
+            g_cnt[threadIdx.x] = 1;
+        }
+        if (!__syncthreads_or(more)) break;
+      }
+      const int link = g_link[s];
+      const int start = block_inclusive_max(link > 0 ? -1 : s, scratch);   // the run's first segment
+      const int mi = (s - start) % p.group_max;
+      const int leader = s - mi;
+      g_size[s] = 1;
+      g_cnt[s] = INT_MAX;
+      __syncthreads();
+      if (mi > 0) {
+        atomicMax(&g_size[leader], mi + 1);
+        atomicMin(&g_cnt[leader], link);
+      }
+      __syncthreads();
+      const int size = g_size[leader];
+      cov = size >= 2 ? g_cnt[leader] : 0;
+      const int ng = (mi == 0 && size >= 2) ? cov : 0;
+      int tot_g;
+      const int og = block_exclusive_scan(ng, scratch, &tot_g);
+      for (int i = 0; i < ng; ++i)
+        if (og + i < p.group_cap) p.group_items[og + i] = make_int4(s, i, size, 0);
+      n_group = min(tot_g, p.group_cap);
+    }
+  }
 
   // pass 1: decode items and partial rows in segment order; prefill item
   // count and cost histogram
@@ -118,16 +234,19 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   int full_base = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
-    const SegInfo si = seg_info(p, s);
+    const SegInfo si = base == 0 && one_chunk ? si0 : seg_info(p, s);
     if (base == 0) first = si;
-    int nd = 0, np = 0, nr = 0;
+    const int cov_s = base == 0 ? cov : 0;
+    int nd = 0, np = 0, nr = 0, nfull = 0;
     if (s < p.num_seqs && !si.ok) {
       status |= 1u;
     } else if (si.ok && si.n >= 1 && si.n <= p.max_decode_n) {
-      nd = (si.L + p.part_tokens - 1) / p.part_tokens;
+      const int parts = (si.L + p.part_tokens - 1) / p.part_tokens;
+      nd = parts - cov_s;
+      nfull = si.L / p.part_tokens - cov_s;
       nr = si.n;
-      if (nd * p.part_tokens > si.L)
-        atomicAdd(&dhist[decode_bucket(si.L - (nd - 1) * p.part_tokens, p.part_tokens)], 1);
+      if (parts * p.part_tokens > si.L)
+        atomicAdd(&dhist[decode_bucket(si.L - (parts - 1) * p.part_tokens, p.part_tokens)], 1);
     } else if (si.ok && si.n > p.max_decode_n) {
       np = (si.n + p.query_tile - 1) / p.query_tile;
       if (!one_chunk)
@@ -135,7 +254,6 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     }
     int tot_d, tot_p, tot_r, tot_f;
     block_exclusive_scan(nd, scratch, &tot_d);
-    const int nfull = nd > 0 ? si.L / p.part_tokens : 0;
     const int ofull = full_base + block_exclusive_scan(nfull, scratch, &tot_f);
     if (base == 0) {
       first_ofull = ofull;
@@ -204,17 +322,18 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     const SegInfo si = base == 0 ? first : seg_info(p, s);
     const bool dec = si.ok && si.n >= 1 && si.n <= p.max_decode_n;
     const int full = dec ? si.L / p.part_tokens : 0;
+    const int cov_s = base == 0 ? cov : 0;   // partitions 0 .. cov_s - 1 are in group items
     int at = first_ofull;
     if (base == 0) {
       full_base = first_tot_f;
     } else {   // more than 1024 segments: place the full partitions again
       int tot_f;
-      at = full_base + block_exclusive_scan(full, scratch, &tot_f);
+      at = full_base + block_exclusive_scan(full - cov_s, scratch, &tot_f);
       full_base += tot_f;
     }
     if (dec) {
-      for (int i = 0; i < full; ++i)
-        if (at + i < p.decode_cap) p.decode_items[at + i] = make_int2(s, i);
+      for (int i = cov_s; i < full; ++i)
+        if (at + i - cov_s < p.decode_cap) p.decode_items[at + i - cov_s] = make_int2(s, i);
       if (si.L > full * p.part_tokens) {
         const int at2 = atomicAdd(&dhist[decode_bucket(si.L - full * p.part_tokens, p.part_tokens)], 1);
         if (at2 < p.decode_cap) p.decode_items[at2] = make_int2(s, full);
@@ -274,6 +393,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     p.hdr->status = any_bad ? 1u : 0u;
     p.hdr->n_decode = min(dec_base, p.decode_cap);
     p.hdr->n_prefill = min(pre_total, p.prefill_cap);
+    p.hdr->n_group = n_group;
     p.hdr->decode_next = 0;
   }
   if (threadIdx.x < kMaxQueues) p.hdr->prefill_next[threadIdx.x] = 0;

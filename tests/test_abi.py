@@ -82,6 +82,10 @@ def test_argument_errors_need_no_gpu(lib):
     # partition knob
     assert lib.paged_attention_set_partition_tokens(48) == 1
     assert lib.paged_attention_set_partition_tokens(0) == 0
+    # shared-prefix group knob
+    assert lib.paged_attention_set_group_members(9) == 1
+    assert lib.paged_attention_set_group_members(-1) == 1
+    assert lib.paged_attention_set_group_members(0) == 0
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

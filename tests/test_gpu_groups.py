@@ -1,0 +1,164 @@
+"""Shared-prefix groups: consecutive single-token decode segments whose
+leading full partitions list the same blocks read those partitions once per
+group instead of once per segment.
+
+Each case runs the same step three ways -- groups of the automatic size,
+groups capped at three members, no groups -- and checks that:
+* the outputs are bitwise the same (a row's MFMA products and softmax do not
+  depend on the other rows of its tile, and a group reads the keys in the
+  order the segment's own item would);
+* the number of group items and of ordinary decode items the plan kernel
+  made (read from the workspace header) equal what a plain Python model of
+  the grouping rule gives;
+* the output matches the CPU oracle within the parity bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_469_amd as pkv
+import workloads
+from gpu_harness import DeviceStep, check_close, down_u16, log
+from oracle import paged
+from workloads.synth import build
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected(wl, part, members):
+    """(group items, ordinary decode items) of the grouping rule: runs of
+    consecutive segments with one new token and more than one partition,
+    linked while their leading full partitions start with the same block id,
+    cut into groups of `members`; a group of two or more covers the
+    partitions every consecutive pair in it links.  (The decode kernel then
+    compares each grouped partition's ids whole.)"""
+    cu, lens, tables = wl.cu_seqlens_q, wl.seq_lens, wl.block_tables
+    n = np.diff(cu)
+    s_count = len(lens)
+    npb = part // 16
+    elig = [bool(n[s] == 1 and lens[s] > part) for s in range(s_count)]
+    link = [0] * s_count
+    for s in range(1, s_count):
+        if elig[s] and elig[s - 1]:
+            full = min(lens[s], lens[s - 1]) // part
+            c = 0
+            while c < full and tables[s, c * npb] == tables[s - 1, c * npb]:
+                c += 1
+            link[s] = c
+    cov = [0] * s_count
+    groups = 0
+    s = 0
+    while s < s_count:
+        e = s + 1
+        while e < s_count and link[e] > 0:
+            e += 1
+        for c0 in range(s, e, members):
+            mem = list(range(c0, min(c0 + members, e)))
+            if len(mem) >= 2:
+                cnt = min(link[m] for m in mem[1:])
+                groups += cnt
+                for m in mem:
+                    cov[m] = cnt
+        s = e
+    max_n = min(8, 32 // (wl.num_q_heads // wl.num_kv_heads))
+    items = sum(-(-int(lens[s]) // part) - cov[s] for s in range(s_count) if 1 <= n[s] <= max_n)
+    return groups, items
+
+
+def _header(ws):
+    h = ws[:64].view(torch.int32).cpu().numpy()
+    return int(h[12]), int(h[1])   # n_group, n_decode
+
+
+def _run(st, members):
+    pkv.paged_attention_set_group_members(members)
+    try:
+        out = st.attend()
+    finally:
+        pkv.paged_attention_set_group_members(0)
+    return down_u16(out), _header(st.ws)
+
+
+def _mixed_runs():
+    """Sharers broken into runs by a 2-token segment and by a short decode of
+    another request; a prefill chunk at the end."""
+    rng = np.random.default_rng([469, 70, 0])
+    segs, rids, sharers = [], [], []
+    for kind, count in (("d", 5), ("spec", 1), ("d", 4), ("short", 1), ("d", 3), ("chunk", 1)):
+        for _ in range(count):
+            r = len(segs)
+            if kind == "d":
+                segs.append((1, int(rng.integers(1100, 2600))))
+                sharers.append(r)
+            elif kind == "spec":
+                segs.append((2, int(rng.integers(1100, 2600))))
+                sharers.append(r)
+            elif kind == "short":
+                segs.append((1, 200))
+            else:
+                segs.append((300, 1000))
+            rids.append(r)
+    return build("mixed_runs", 4, 32, 8, 128, segs, request_ids=rids, shared_prefix=1024,
+                 shared_requests=tuple(sharers), num_blocks=2000)
+
+
+CASES = {
+    # 8B-shaped continuous-batching step: 19 sharers (groups of 8, 8, 3)
+    "cb_8b_p256": (lambda: workloads.make("cb_step_8b", num_decodes=40, ctx=(1100, 3000), shared=19,
+                                          prefix=1024, chunk=300, chunk_history=700), 256, None),
+    "cb_8b_p1024": (lambda: workloads.make("cb_step_8b", num_decodes=30, ctx=(1100, 3000), shared=12,
+                                           prefix=1024, chunk=300, chunk_history=700), 1024, None),
+    # 70B-shaped heads (G = 8: groups of 4)
+    "g8_70b": (lambda: build("g8_70b", 5, 64, 8, 128, [(1, 2100 + 37 * i) for i in range(11)],
+                             shared_prefix=2048, shared_requests=tuple(range(9))), 512, None),
+    # G = 1, head_dim 64: eight members in one column tile
+    "g1_d64": (lambda: build("g1_d64", 4, 8, 8, 64, [(1, 700 + 13 * i) for i in range(12)],
+                             shared_prefix=512, shared_requests=tuple(range(12))), 128, None),
+    # G = 16: groups of two
+    "g16": (lambda: build("g16", 4, 32, 2, 128, [(1, 600 + 5 * i) for i in range(7)],
+                          shared_prefix=512, shared_requests=tuple(range(7))), 256, None),
+    # a shared prefix of 20 partitions: the plan compares 8 per round
+    "long_prefix": (lambda: build("long_prefix", 2, 32, 8, 128, [(1, 2600 + 41 * i) for i in range(10)],
+                                  shared_prefix=2560, shared_requests=tuple(range(10))), 128, None),
+    # exactly 8 shared partitions and 8 full ones per member: a round boundary
+    "round_edge": (lambda: build("round_edge", 2, 32, 8, 128, [(1, 1030 + 11 * i) for i in range(9)],
+                                 shared_prefix=1024, shared_requests=tuple(range(9))), 128, None),
+    # runs broken by a non-member; two members whose third partition holds a
+    # copy of a shared block (same data, another id): at the partition's
+    # first entry (the plan's links stop there) and inside it (the decode
+    # kernel finds it and computes that member's partition on its own)
+    "mixed_runs": (_mixed_runs, 256, [(11, 2 * 16), (7, 2 * 16 + 3)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_groups_bitwise_and_parity(name):
+    make, part, copy = CASES[name]
+    wl = make()
+    st = DeviceStep(wl, host_pool=True)
+    for s, idx in copy or []:   # point a member's table entry at a copy of its block
+        used = set(int(x) for x in wl.block_tables[wl.block_tables >= 0].ravel())
+        spare = next(b for b in range(wl.num_blocks) if b not in used)
+        src = int(wl.block_tables[s, idx])
+        st.pool[spare].copy_(st.pool[src])
+        st.host[spare] = st.host[src]
+        wl.block_tables[s, idx] = spare
+        st.bt = torch.from_numpy(wl.block_tables).cuda()
+    group = wl.num_q_heads // wl.num_kv_heads
+    auto = min(8, 32 // group)
+    log(f"case groups {name}: S={wl.num_seqs} T={wl.num_tokens} G={group} P={part}")
+    pkv.paged_attention_set_partition_tokens(part)
+    try:
+        runs = {m: _run(st, m) for m in (0, 3, 1)}
+    finally:
+        pkv.paged_attention_set_partition_tokens(0)
+    for m, (out, (n_group, n_decode)) in runs.items():
+        want = _expected(wl, part, auto if m == 0 else min(auto, m))
+        log(f"  members {m}: {n_group} group items, {n_decode} decode items (expected {want})")
+        assert (n_group, n_decode) == want, f"members {m}"
+        assert np.array_equal(out, runs[1][0]), f"members {m}: output differs from the ungrouped run"
+    assert runs[0][1][0] > 0, "the case must form groups"
+    assert pkv.paged_attention_device_status(st.ws) == 0
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens, wl.scale)
+    check_close(runs[0][0], ref, f"groups {name}")
