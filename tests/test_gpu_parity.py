@@ -253,12 +253,15 @@ def test_bad_metadata_is_skipped_and_flagged():
 
 # ------------------------------------------------------------------ full size
 
-def _full_sampled(wl, sample_segments, rows_per_segment=None, pool_blocks=None, fill_others=False):
+def _full_sampled(wl, sample_segments, rows_per_segment=None, pool_blocks=None, fill_others=False,
+                  ungrouped_equal=False):
     """Full-size workload.  Each request's K/V is written with one
     paged_kv_write call over all its positions (the step's write order is
     covered by the reduced cases).  With ``fill_others`` only the sampled
     segments' values come from the host generator; the others are drawn on
-    the GPU (seeded) and are not compared."""
+    the GPU (seeded) and are not compared.  With ``ungrouped_equal`` the step
+    is run again without shared-prefix groups and the whole output must be
+    bitwise the same."""
     torch.cuda.empty_cache()
     hkv, d = wl.num_kv_heads, wl.head_dim
     nb = wl.num_blocks if pool_blocks is None else pool_blocks
@@ -285,6 +288,15 @@ def _full_sampled(wl, sample_segments, rows_per_segment=None, pool_blocks=None, 
                               up(wl.seq_lens), wl.scale, workspace=ws)
     torch.cuda.synchronize()
     assert pkv.paged_attention_device_status(ws) == 0
+    if ungrouped_equal:
+        pkv.paged_attention_set_group_members(1)
+        try:
+            again = pkv.paged_attention(up(q_host), pool, up(wl.block_tables), up(wl.cu_seqlens_q),
+                                        up(wl.seq_lens), wl.scale, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            pkv.paged_attention_set_group_members(0)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16)), "groups change the output"
     # write check on the sampled requests: their blocks hold exactly their K/V
     for s in sample:
         length = int(wl.seq_lens[s])
@@ -322,7 +334,10 @@ def test_full_cb_step_8b():
     wl = workloads.make("cb_step_8b")
     log(f"case full cb_step_8b: T={wl.num_tokens}")
     chunk = wl.num_seqs - 1
-    got, ref = _full_sampled(wl, [0, 1, 63, 64, 150, chunk], rows_per_segment=24)
+    # segments 0, 1 and 63 share the cached prefix: grouped (and the whole
+    # output equals the ungrouped run's, bit for bit)
+    got, ref = _full_sampled(wl, [0, 1, 63, 64, 150, chunk], rows_per_segment=24,
+                             ungrouped_equal=True)
     check_close(got, ref, "cb_step_8b full (5 decodes + 26 chunk rows)")
 
 
