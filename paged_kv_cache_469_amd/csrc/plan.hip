@@ -147,14 +147,12 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   int cov = 0;       // leading partitions of the thread's segment that group items cover
   int n_group = 0;
   const bool grouping = one_chunk && p.group_max >= 2;
-  // the segment's first table entry is loaded in the same trip as its bounds
-  const int fb = grouping && (int)threadIdx.x < p.num_seqs && p.width > 0
-                     ? p.bt[(int64_t)threadIdx.x * p.width] : 0;
   if (one_chunk) si0 = seg_info(p, threadIdx.x);
   if (grouping) {
     const int s = threadIdx.x;
     const bool elig = si0.ok && si0.n == 1 && si0.L > p.part_tokens;
-    g_fb[s] = elig ? fb : 0;
+    // a table entry is read only below ceil(L / 16)
+    g_fb[s] = elig ? p.bt[(int64_t)s * p.width] : 0;
     g_len[s] = elig ? si0.L : 0;   // 0: not eligible
     g_link[s] = 0;
     __syncthreads();
