@@ -11,6 +11,8 @@ groups capped at three members, no groups -- and checks that:
   made (read from the workspace header) equal what a plain Python model of
   the grouping rule gives;
 * the output matches the CPU oracle within the parity bound.
+Random sharing patterns (runs, prefix depths, copied blocks, segments of 0
+or 2 new tokens, short contexts) are checked the same way.
 """
 
 import numpy as np
@@ -19,8 +21,8 @@ import torch
 
 import paged_kv_cache_469_amd as pkv
 import workloads
-from gpu_harness import DeviceStep, check_close, down_u16, log
-from oracle import paged
+from gpu_harness import DeviceStep, check_close, down_u16, log, up
+from oracle import bf16, paged
 from workloads.synth import build
 
 pytestmark = pytest.mark.gpu
@@ -162,3 +164,77 @@ def test_groups_bitwise_and_parity(name):
     assert pkv.paged_attention_device_status(st.ws) == 0
     ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens, wl.scale)
     check_close(runs[0][0], ref, f"groups {name}")
+
+
+def _random_step(seed, hq=32, hkv=8, d=128, part=128):
+    """Random sharing: runs of segments share a random number of leading
+    blocks; some entries point at copies of the shared block (same data,
+    another id); some segments have 0 or 2 new tokens or a short context."""
+    from types import SimpleNamespace
+    rng = np.random.default_rng([469, 71, seed])
+    s_count = int(rng.integers(20, 40))
+    n = rng.choice([1, 1, 1, 1, 1, 1, 0, 2], size=s_count)
+    lens = rng.integers(part // 2, 6 * part, size=s_count)
+    lens = np.maximum(lens, n).astype(np.int32)
+    width = int(-(-lens.max() // 16))
+    tables = np.full((s_count, width), -1, dtype=np.int32)
+    next_id = 0
+    prefix = []
+    copies = []   # (copy id, original id)
+    for s in range(s_count):
+        nblk = -(-int(lens[s]) // 16)
+        if rng.random() < 0.25 or not prefix:   # a new run with a fresh shared prefix
+            prefix = list(range(next_id, next_id + int(rng.integers(1, 30))))
+            next_id += len(prefix)
+        k = min(len(prefix), nblk)
+        row = prefix[:k] + list(range(next_id, next_id + nblk - k))
+        next_id += nblk - k
+        for _ in range(int(rng.integers(0, 2))):   # a copied entry inside the shared part
+            if k:
+                i = int(rng.integers(0, k))
+                copies.append((next_id, row[i]))
+                row[i] = next_id
+                next_id += 1
+        tables[s, :nblk] = row
+    nb = next_id
+    pool = bf16.f32_to_bf16(rng.standard_normal((nb, 2, 16, hkv, d)).astype(np.float32))
+    for c, o in copies:
+        pool[c] = pool[o]
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = bf16.f32_to_bf16(rng.standard_normal((int(cu[-1]), hq, d)).astype(np.float32))
+    wl = SimpleNamespace(cu_seqlens_q=cu, seq_lens=lens, block_tables=tables, num_q_heads=hq,
+                         num_kv_heads=hkv, scale=float(np.float32(1 / np.sqrt(d))))
+    return wl, pool, q, part
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_groups_random_tables(seed):
+    wl, pool, q, part = _random_step(seed)
+    s_count, t = len(wl.seq_lens), int(wl.cu_seqlens_q[-1])
+    log(f"case groups random seed {seed}: S={s_count} T={t} NB={pool.shape[0]}")
+    dev = {k: up(v) for k, v in (("pool", pool), ("q", q), ("bt", wl.block_tables),
+                                   ("cu", wl.cu_seqlens_q), ("lens", wl.seq_lens))}
+    ws = torch.empty(pkv.paged_attention_workspace_size(s_count, t, wl.num_q_heads, wl.num_kv_heads,
+                                                        pool.shape[-1], wl.block_tables.shape[1]),
+                     dtype=torch.uint8, device="cuda")
+    auto = min(8, 32 // (wl.num_q_heads // wl.num_kv_heads))
+    outs = {}
+    pkv.paged_attention_set_partition_tokens(part)
+    try:
+        for m in (0, 3, 1):
+            pkv.paged_attention_set_group_members(m)
+            o = pkv.paged_attention(dev["q"], dev["pool"], dev["bt"], dev["cu"], dev["lens"], wl.scale,
+                                    workspace=ws)
+            torch.cuda.synchronize()
+            outs[m] = (down_u16(o), _header(ws))
+            assert pkv.paged_attention_device_status(ws) == 0
+    finally:
+        pkv.paged_attention_set_group_members(0)
+        pkv.paged_attention_set_partition_tokens(0)
+    for m, (out, counts) in outs.items():
+        want = _expected(wl, part, auto if m == 0 else min(auto, m))
+        log(f"  members {m}: {counts[0]} group items, {counts[1]} decode items (expected {want})")
+        assert counts == want
+        assert np.array_equal(out, outs[1][0]), f"members {m}: output differs from the ungrouped run"
+    ref = paged.attend(q, pool, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens, wl.scale)
+    check_close(outs[0][0], ref, f"groups random seed {seed}")
