@@ -108,7 +108,7 @@ Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int
   off = align256(off + (size_t)num_seqs * sizeof(int32_t));
   l.group_cap = l.decode_cap / 2 + 1;
   l.group_items = off;
-  off = align256(off + (size_t)l.group_cap * sizeof(int4));
+  off = align256(off + (size_t)l.group_cap * sizeof(pkv::GroupItem));
   l.part_ml = off;
   off = align256(off + (size_t)l.rows_cap * l.pmax * hq * sizeof(float2));
   l.part_o = off;
@@ -269,7 +269,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   pp.seg_row = reinterpret_cast<int32_t*>(ws + l.seg_row);
   pp.max_decode_n = max_decode_tokens(group);
   pp.rows_cap = (int32_t)l.rows_cap;
-  pp.group_items = reinterpret_cast<int4*>(ws + l.group_items);
+  pp.group_items = reinterpret_cast<pkv::GroupItem*>(ws + l.group_items);
   pp.group_cap = (int32_t)l.group_cap;
   pp.group_max = group_members(group);
   e = stage(0, stream);

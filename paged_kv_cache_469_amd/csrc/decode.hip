@@ -313,25 +313,28 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int pa
                      row_bytes, block_bytes);
 }
 
-// Group item (segments s0 .. s0 + nmem - 1, partition part, KV head g) of
-// single-token decode segments that the plan found to share this full
-// partition (by its first block id): each member's block ids of the
-// partition are compared with the first member's, and the keys are read once
-// for all members that match.  Row 16c + m is (member mi, head hh) and sees
-// all P keys (each member's token comes after them); results go to each
-// member's own partial row.  A member whose ids differ is computed on its own
-// afterwards, from its own table.
+// Group item (partition part of the member segments gi.seg[0 .. nmem - 1],
+// KV head g): single-token decode segments that the plan found to share
+// this full partition (by its first block id): each member's block ids of
+// the partition are compared with the first member's, and the keys are read
+// once for all members that match.  Row 16c + m is (member mi, head hh) and
+// sees all P keys (each member's token comes after them); results go to
+// each member's own partial row.  A member whose ids differ is computed on
+// its own afterwards, from its own table.
 template <int D, int CT>
-__device__ __forceinline__ void group_item(const DecodeParams& p, int s0, int part, int nmem, int g,
+__device__ __forceinline__ void group_item(const DecodeParams& p, const GroupItem& gi, int g,
                                            int lane, int64_t row_bytes, int64_t block_bytes) {
+  const int part = gi.part;
+  const int nmem = gi.nmem;
   const int key0 = part * p.part_tokens;
   const int key1 = key0 + p.part_tokens;
   const int npb = p.part_tokens / kBlock;   // <= 64: one id per lane
-  const int32_t* first = p.bt + (int64_t)s0 * p.width + key0 / kBlock;
   int ids[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    ids[i] = lane < npb ? first[(int64_t)min(i, nmem - 1) * p.width + lane] : 0;
+  for (int i = 0; i < 8; ++i) {
+    const int32_t* row = p.bt + (int64_t)gi.seg[i] * p.width + key0 / kBlock;
+    ids[i] = (i < nmem && lane < npb) ? row[lane] : 0;
+  }
   uint32_t differ = 0;
 #pragma unroll
   for (int i = 1; i < 8; ++i)
@@ -341,7 +344,10 @@ __device__ __forceinline__ void group_item(const DecodeParams& p, int s0, int pa
   for (int c = 0; c < CT; ++c) {
     const int row = 16 * c + (lane & 15);
     const int mi = row / p.group;
-    const int sm = s0 + min(mi, nmem - 1);
+    int sm = gi.seg[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+      if (mi == i) sm = gi.seg[i];
     const int r0 = p.seg_row[sm];
     rm.live[c] = mi < nmem && r0 >= 0 && !((differ >> mi) & 1u);
     rm.kend[c] = key1;
@@ -349,12 +355,15 @@ __device__ __forceinline__ void group_item(const DecodeParams& p, int s0, int pa
     rm.hq[c] = g * p.group + (row - mi * p.group);
     rm.prow[c] = r0;
   }
-  decode_rows<D, CT>(p, p.bt + (int64_t)s0 * p.width, key0, key1, part, false, g, lane, rm,
+  decode_rows<D, CT>(p, p.bt + (int64_t)gi.seg[0] * p.width, key0, key1, part, false, g, lane, rm,
                      row_bytes, block_bytes);
   while (differ) {
     const int mi = __builtin_ctz(differ);
     differ &= differ - 1;
-    const int sm = s0 + mi;
+    int sm = gi.seg[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+      if (mi == i) sm = gi.seg[i];
     const int hh = lane & 15;
     RowMap<1> one;
     one.live[0] = hh < p.group && p.seg_row[sm] >= 0;
@@ -384,12 +393,12 @@ decode_kernel(DecodeParams p) {
     it = wave_uniform(__shfl(it, 0));
     if (it >= n_items) break;
     if (it < n_grp) {
-      const int4 gi = p.groups[it / p.hkv];
+      const GroupItem gi = p.groups[it / p.hkv];
       const int g = it % p.hkv;
-      if (gi.z * p.group <= 16)
-        group_item<D, 1>(p, gi.x, gi.y, gi.z, g, lane, row_bytes, block_bytes);
+      if (gi.nmem * p.group <= 16)
+        group_item<D, 1>(p, gi, g, lane, row_bytes, block_bytes);
       else
-        group_item<D, 2>(p, gi.x, gi.y, gi.z, g, lane, row_bytes, block_bytes);
+        group_item<D, 2>(p, gi, g, lane, row_bytes, block_bytes);
       continue;
     }
     it -= n_grp;

@@ -19,6 +19,16 @@ struct PrefillItem {
 };
 static_assert(sizeof(PrefillItem) == 64, "one scalar load of 16 dwords");
 
+// One shared-prefix group work entry: a partition that its members (single-
+// token decode segments, listed in seg[0 .. nmem - 1]) all hold in the same
+// blocks.
+struct GroupItem {
+  int32_t part, nmem;
+  int32_t pad[2];
+  int32_t seg[8];
+};
+static_assert(sizeof(GroupItem) == 48, "three 16-byte lines");
+
 struct PlanParams {
   const int32_t* cu;
   const int32_t* lens;
@@ -27,7 +37,7 @@ struct PlanParams {
   int2* decode_items;
   PrefillItem* prefill_items;
   int32_t* seg_row;      // per segment: first partial row of a decode segment, else -1
-  int4* group_items;     // shared-prefix groups: (first segment, partition, members, 0)
+  GroupItem* group_items;   // shared-prefix groups
   int32_t num_seqs;
   int32_t num_tokens;
   int32_t width;         // block-table row length
@@ -54,7 +64,7 @@ struct DecodeParams {
   const int32_t* seg_row;  // per segment: its first partial row (token 0), -1 if not decode
   WsHeader* hdr;
   const int2* items;       // (segment, partition)
-  const int4* groups;      // (first segment, partition, members, 0), taken before items
+  const GroupItem* groups; // shared-prefix groups, taken before items
   int64_t q_stride;
   int64_t num_blocks;
   int32_t width;           // block table row length

@@ -84,6 +84,42 @@ __device__ int block_inclusive_max(int v, int* scratch) {
   return res;
 }
 
+// Value of lane (lane ^ J) of the wave: a quad permutation (DPP) for J = 1
+// and 2, a swizzle within 32 lanes for J = 4 .. 16, a permute for J = 32.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  } else if constexpr (J < 32) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (J << 10));   // and 31, xor J
+  } else {
+    return __shfl_xor(x, J);
+  }
+}
+
+// One compare-exchange stage of a bitonic sort with the partner at distance
+// J: the lower position of a pair keeps the smaller key in an ascending
+// block ((pos & k) == 0), the larger in a descending one.
+template <int J>
+__device__ __forceinline__ uint32_t bitonic_lane_stage(uint32_t key, int pos, int k) {
+  const uint32_t other = lane_xor<J>(key);
+  const bool lower = (pos & J) == 0;
+  const bool ascending = (pos & k) == 0;
+  return (lower == ascending) ? min(key, other) : max(key, other);
+}
+
+// The stages of block size k whose partners are in the same wave (J < 64).
+__device__ __forceinline__ uint32_t bitonic_wave_stages(uint32_t key, int pos, int k) {
+  if (k > 32) key = bitonic_lane_stage<32>(key, pos, k);
+  if (k > 16) key = bitonic_lane_stage<16>(key, pos, k);
+  if (k > 8) key = bitonic_lane_stage<8>(key, pos, k);
+  if (k > 4) key = bitonic_lane_stage<4>(key, pos, k);
+  if (k > 2) key = bitonic_lane_stage<2>(key, pos, k);
+  return bitonic_lane_stage<1>(key, pos, k);
+}
+
 struct SegInfo {
   int n, L, c0;
   bool ok;
@@ -125,8 +161,14 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   // wave per segment spreads its query tiles over the lanes
   __shared__ int pl_seg[1024], pl_n[1024], pl_len[1024], pl_c0[1024];
   __shared__ int pl_count;
-  // shared-prefix grouping of a batch of at most 1024 segments
-  __shared__ int g_fb[1024], g_len[1024], g_link[1024], g_cand[1024], g_size[1024], g_cnt[1024];
+  // shared-prefix grouping of a batch of at most 1024 segments: a 2048-slot
+  // hash set of first table entries (its storage then holds the sort keys), per segment its
+  // length and covered partitions, per sorted position its segment, length,
+  // link and group scratch
+  __shared__ int g_hash[2048];
+  uint32_t* g_key = (uint32_t*)g_hash;   // the sort keys reuse the hash set's storage
+  __shared__ int g_lseg[1024], g_cov[1024];
+  __shared__ int g_seg[1024], g_len[1024], g_link[1024], g_cand[1024], g_size[1024], g_cnt[1024];
   const bool one_chunk = p.num_seqs <= 1024;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -135,14 +177,17 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   if (threadIdx.x < 16) p.hdr->zeros[threadIdx.x] = 0u;
   __syncthreads();
 
-  // pass 0: shared-prefix groups.  Consecutive single-token decode segments
-  // of more than one partition whose leading full partitions start with the
-  // same block ids (a cached prefix the block manager shares, "vLLM 学习笔记
-  // 01", section 2.2) form runs; each run is cut into groups of at most
-  // group_max members, and a group reads each partition that all its
-  // members share once, for all of them (one group item per partition).
-  // Those partitions leave the members' own item lists.  A first table
-  // entry equal to the previous segment's makes a candidate.
+  // pass 0: shared-prefix groups.  Single-token decode segments of more
+  // than one partition whose leading full partitions start with the same
+  // block ids (a cached prefix the block manager shares, "vLLM 学习笔记 01",
+  // section 2.2) are grouped whatever their order in the batch: the
+  // eligible segments are sorted by (first table entry, index), neighbours
+  // in that order that share leading partitions form runs, each run is cut
+  // into groups of at most group_max members, and a group reads each
+  // partition that all its members share once, for all of them (one group
+  // item per partition).  Those partitions leave the members' own item
+  // lists.  A hash set of the first entries finds whether any two are equal
+  // at all; only then is the batch sorted.
   SegInfo si0{0, 0, 0, false};
   int cov = 0;       // leading partitions of the thread's segment that group items cover
   int n_group = 0;
@@ -150,26 +195,78 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   if (one_chunk) si0 = seg_info(p, threadIdx.x);
   if (grouping) {
     const int s = threadIdx.x;
-    const bool elig = si0.ok && si0.n == 1 && si0.L > p.part_tokens;
+    const bool elig0 = si0.ok && si0.n == 1 && si0.L > p.part_tokens;
     // a table entry is read only below ceil(L / 16)
-    g_fb[s] = elig ? p.bt[(int64_t)s * p.width] : 0;
-    g_len[s] = elig ? si0.L : 0;   // 0: not eligible
-    g_link[s] = 0;
+    const int fb = elig0 ? p.bt[(int64_t)s * p.width] : -1;
+    const bool elig = elig0 && fb >= 0;
+    g_hash[s] = -1;
+    g_hash[s + 1024] = -1;
+    g_lseg[s] = si0.L;
+    g_cov[s] = 0;
     __syncthreads();
-    const bool cand = elig && s > 0 && g_len[s - 1] > 0 && g_fb[s] == g_fb[s - 1];
-    if (__syncthreads_or(cand)) {   // else no group: nothing more to do
+    bool dup = false;
+    uint32_t h = 2048;   // the slot of the segment's first entry (2048: not eligible)
+    if (elig) {   // open addressing over 2048 slots for at most 1024 keys: always ends
+      h = ((uint32_t)fb * 2654435761u) >> 21;
+      for (;;) {
+        const int old = atomicCAS(&g_hash[h], -1, fb);
+        if (old == -1) break;
+        if (old == fb) {
+          dup = true;
+          break;
+        }
+        h = (h + 1) & 2047u;
+      }
+    }
+    // each distinct first entry owns one slot, so equal slots mean equal
+    // first entries; sorting by (slot, index) keeps the segments of one
+    // first entry together, in index order
+    if (__syncthreads_or(dup)) {
+      // bitonic sort of (slot, index) over the first nsort positions (a
+      // power of two >= the segment count; ineligible segments sort last).
+      // Thread s holds position s; its partner s ^ j is in the same wave for
+      // j < 64 (exchange by lane shuffle), else in LDS.
+      int nsort = 2;
+      while (nsort < p.num_seqs) nsort <<= 1;
+      __syncthreads();   // the hash set's storage becomes the key array
+      uint32_t key = (h << 10) | (uint32_t)s;
+      for (int k = 2; k <= nsort; k <<= 1) {
+        for (int j = k >> 1; j >= 64; j >>= 1) {
+          g_key[s] = key;
+          __syncthreads();
+          const uint32_t other = g_key[s ^ j];
+          __syncthreads();
+          // the lower position of a pair keeps the smaller key in an
+          // ascending block ((s & k) == 0), the larger in a descending one
+          const bool lower = (s & j) == 0;
+          const bool ascending = (s & k) == 0;
+          key = (lower == ascending) ? min(key, other) : max(key, other);
+        }
+        key = bitonic_wave_stages(key, s, k);
+      }
+      g_key[s] = key;
+      __syncthreads();
+      // thread r now works on sorted position r
+      const int r = s;   // its key is `key` (g_key[r])
+      const bool relig = (key >> 10) < 2048u;
+      const int seg = (int)(key & 1023u);
+      g_seg[r] = seg;
+      g_len[r] = relig ? g_lseg[seg] : 0;   // 0: not eligible
+      g_link[r] = 0;
+      __syncthreads();
+      const bool cand = relig && r > 0 && g_len[r - 1] > 0 && (g_key[r - 1] >> 10) == (key >> 10);
       int ncand;
       const int ci = block_exclusive_scan(cand ? 1 : 0, scratch, &ncand);
-      if (cand) g_cand[ci] = s;
+      if (cand) g_cand[ci] = r;
       __syncthreads();
-      // link of each candidate: how many leading full partitions it has whose
-      // first block ids equal the previous segment's.  Only the first id of
-      // a partition is compared here (one pair of loads per partition, all
-      // in one trip to memory); the decode kernel compares a grouped
-      // partition's ids whole and computes a member that differs on its own.
-      // Rounds of 8 partitions: a unit is (candidate, partition); g_size
-      // holds a candidate's first differing partition, g_cnt marks finished
-      // candidates.
+      // link of each candidate position: how many leading full partitions
+      // its segment has whose first block ids equal the previous position's.
+      // Only the first id of a partition is compared here (one pair of loads
+      // per partition, all in one trip to memory); the decode kernel compares
+      // a grouped partition's ids whole and computes a member that differs
+      // on its own.  Rounds of 8 partitions: a unit is (candidate,
+      // partition); g_size holds a candidate's first differing partition,
+      // g_cnt marks finished candidates.
       constexpr int kRound = 8;
       const int npb = p.part_tokens / kBlock;   // block ids per partition
       if ((int)threadIdx.x < ncand) g_cnt[threadIdx.x] = 0;
@@ -179,13 +276,14 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
         for (int u = threadIdx.x; u < ncand * kRound; u += 1024) {
           const int k = u / kRound;
           if (g_cnt[k]) continue;
-          const int sc = g_cand[k];
+          const int rc = g_cand[k];
           const int c = c0 + u % kRound;
           // a partition counts when it is full in both segments
-          bool differ = c >= min(g_len[sc], g_len[sc - 1]) / p.part_tokens;
+          bool differ = c >= min(g_len[rc], g_len[rc - 1]) / p.part_tokens;
           if (!differ) {
-            const int32_t* a = p.bt + (int64_t)sc * p.width + c * npb;
-            differ = a[0] != a[-(int64_t)p.width];
+            const int32_t* a = p.bt + (int64_t)g_seg[rc] * p.width + c * npb;
+            const int32_t* b = p.bt + (int64_t)g_seg[rc - 1] * p.width + c * npb;
+            differ = a[0] != b[0];
           }
           if (differ) atomicMin(&g_size[k], c);
         }
@@ -201,12 +299,12 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
         }
         if (!__syncthreads_or(more)) break;
       }
-      const int link = g_link[s];
-      const int start = block_inclusive_max(link > 0 ? -1 : s, scratch);   // the run's first segment
-      const int mi = (s - start) % p.group_max;
-      const int leader = s - mi;
-      g_size[s] = 1;
-      g_cnt[s] = INT_MAX;
+      const int link = g_link[r];
+      const int start = block_inclusive_max(link > 0 ? -1 : r, scratch);   // the run's first position
+      const int mi = (r - start) % p.group_max;
+      const int leader = r - mi;
+      g_size[r] = 1;
+      g_cnt[r] = INT_MAX;
       __syncthreads();
       if (mi > 0) {
         atomicMax(&g_size[leader], mi + 1);
@@ -214,13 +312,23 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       }
       __syncthreads();
       const int size = g_size[leader];
-      cov = size >= 2 ? g_cnt[leader] : 0;
-      const int ng = (mi == 0 && size >= 2) ? cov : 0;
+      const int my_cov = size >= 2 ? g_cnt[leader] : 0;
+      if (my_cov > 0) g_cov[seg] = my_cov;
+      const int ng = (mi == 0 && size >= 2) ? my_cov : 0;
       int tot_g;
       const int og = block_exclusive_scan(ng, scratch, &tot_g);
-      for (int i = 0; i < ng; ++i)
-        if (og + i < p.group_cap) p.group_items[og + i] = make_int4(s, i, size, 0);
+      if (ng > 0) {
+        GroupItem gi{};
+        gi.nmem = size;
+        for (int i = 0; i < 8; ++i) gi.seg[i] = g_seg[r + min(i, size - 1)];
+        for (int i = 0; i < ng; ++i) {
+          gi.part = i;
+          if (og + i < p.group_cap) p.group_items[og + i] = gi;
+        }
+      }
       n_group = min(tot_g, p.group_cap);
+      __syncthreads();
+      cov = g_cov[s];
     }
   }
 

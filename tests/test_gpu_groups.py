@@ -29,40 +29,43 @@ pytestmark = pytest.mark.gpu
 
 
 def _expected(wl, part, members):
-    """(group items, ordinary decode items) of the grouping rule: runs of
-    consecutive segments with one new token and more than one partition,
-    linked while their leading full partitions start with the same block id,
-    cut into groups of `members`; a group of two or more covers the
-    partitions every consecutive pair in it links.  (The decode kernel then
-    compares each grouped partition's ids whole.)"""
+    """(group items, ordinary decode items) of the grouping rule: the
+    segments with one new token, more than one partition and a valid first
+    block id, sorted by (first block id, index); neighbours in that order
+    link while their leading full partitions start with the same block id;
+    runs of links are cut into groups of `members`, and a group of two or
+    more covers the partitions every neighbouring pair in it links.  (The
+    decode kernel then compares each grouped partition's ids whole.)"""
     cu, lens, tables = wl.cu_seqlens_q, wl.seq_lens, wl.block_tables
     n = np.diff(cu)
     s_count = len(lens)
     npb = part // 16
-    elig = [bool(n[s] == 1 and lens[s] > part) for s in range(s_count)]
-    link = [0] * s_count
-    for s in range(1, s_count):
-        if elig[s] and elig[s - 1]:
-            full = min(lens[s], lens[s - 1]) // part
+    order = sorted((s for s in range(s_count) if n[s] == 1 and lens[s] > part and tables[s, 0] >= 0),
+                   key=lambda s: (int(tables[s, 0]), s))
+    link = [0] * len(order)
+    for r in range(1, len(order)):
+        a, b = order[r], order[r - 1]
+        if tables[a, 0] == tables[b, 0]:
+            full = min(lens[a], lens[b]) // part
             c = 0
-            while c < full and tables[s, c * npb] == tables[s - 1, c * npb]:
+            while c < full and tables[a, c * npb] == tables[b, c * npb]:
                 c += 1
-            link[s] = c
+            link[r] = c
     cov = [0] * s_count
     groups = 0
-    s = 0
-    while s < s_count:
-        e = s + 1
-        while e < s_count and link[e] > 0:
+    r = 0
+    while r < len(order):
+        e = r + 1
+        while e < len(order) and link[e] > 0:
             e += 1
-        for c0 in range(s, e, members):
+        for c0 in range(r, e, members):
             mem = list(range(c0, min(c0 + members, e)))
             if len(mem) >= 2:
                 cnt = min(link[m] for m in mem[1:])
                 groups += cnt
                 for m in mem:
-                    cov[m] = cnt
-        s = e
+                    cov[order[m]] = cnt
+        r = e
     max_n = min(8, 32 // (wl.num_q_heads // wl.num_kv_heads))
     items = sum(-(-int(lens[s]) // part) - cov[s] for s in range(s_count) if 1 <= n[s] <= max_n)
     return groups, items
@@ -120,6 +123,9 @@ CASES = {
     # G = 16: groups of two
     "g16": (lambda: build("g16", 4, 32, 2, 128, [(1, 600 + 5 * i) for i in range(7)],
                           shared_prefix=512, shared_requests=tuple(range(7))), 256, None),
+    # sharers interleaved with other requests (every third segment shares)
+    "interleaved": (lambda: build("interleaved", 4, 32, 8, 128, [(1, 1100 + 29 * i) for i in range(30)],
+                                  shared_prefix=1024, shared_requests=tuple(range(0, 30, 3))), 256, None),
     # a shared prefix of 20 partitions: the plan compares 8 per round
     "long_prefix": (lambda: build("long_prefix", 2, 32, 8, 128, [(1, 2600 + 41 * i) for i in range(10)],
                                   shared_prefix=2560, shared_requests=tuple(range(10))), 128, None),
@@ -166,10 +172,12 @@ def test_groups_bitwise_and_parity(name):
     check_close(runs[0][0], ref, f"groups {name}")
 
 
-def _random_step(seed, hq=32, hkv=8, d=128, part=128):
+def _random_step(seed, hq=32, hkv=8, d=128, part=128, shuffle=False):
     """Random sharing: runs of segments share a random number of leading
     blocks; some entries point at copies of the shared block (same data,
-    another id); some segments have 0 or 2 new tokens or a short context."""
+    another id); some segments have 0 or 2 new tokens or a short context.
+    With ``shuffle`` the segments are packed in a random order, so requests
+    that share a prefix are interleaved with others."""
     from types import SimpleNamespace
     rng = np.random.default_rng([469, 71, seed])
     s_count = int(rng.integers(20, 40))
@@ -196,6 +204,9 @@ def _random_step(seed, hq=32, hkv=8, d=128, part=128):
                 row[i] = next_id
                 next_id += 1
         tables[s, :nblk] = row
+    if shuffle:
+        perm = rng.permutation(s_count)
+        n, lens, tables = n[perm], lens[perm], tables[perm]
     nb = next_id
     pool = bf16.f32_to_bf16(rng.standard_normal((nb, 2, 16, hkv, d)).astype(np.float32))
     for c, o in copies:
@@ -207,9 +218,9 @@ def _random_step(seed, hq=32, hkv=8, d=128, part=128):
     return wl, pool, q, part
 
 
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(8))
 def test_groups_random_tables(seed):
-    wl, pool, q, part = _random_step(seed)
+    wl, pool, q, part = _random_step(seed, shuffle=seed >= 4)
     s_count, t = len(wl.seq_lens), int(wl.cu_seqlens_q[-1])
     log(f"case groups random seed {seed}: S={s_count} T={t} NB={pool.shape[0]}")
     dev = {k: up(v) for k, v in (("pool", pool), ("q", q), ("bt", wl.block_tables),
