@@ -165,10 +165,11 @@ int paged_attention_device_status(const void* workspace, uint32_t* status,
 int paged_attention_set_partition_tokens(int32_t tokens);
 
 /* Most members of a shared-prefix group ("vLLM 学习笔记 01", section 2.2:
- * requests with a common cached prefix hold the same blocks).  Consecutive
- * single-token decode segments whose leading full partitions list the same
- * block ids are grouped, and a group reads each shared partition once for
- * all its members instead of once per member.  0 = automatic (the default:
+ * requests with a common cached prefix hold the same blocks).  Single-token
+ * decode segments whose leading full partitions list the same block ids are
+ * grouped, wherever they sit in the batch (calls of at most 1024 segments),
+ * and a group reads each shared partition once for all its members instead
+ * of once per member.  0 = automatic (the default:
  * min(8, 32 / G) members), 1 = no grouping, 2..8 = at most that many (never
  * more than 32 / G).  Results are bitwise the same either way; a knob for
  * measurements.  Process-wide; returns PAGED_EINVAL for other values. */
