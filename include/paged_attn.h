@@ -167,7 +167,7 @@ int paged_attention_set_partition_tokens(int32_t tokens);
 /* Most members of a shared-prefix group ("vLLM 学习笔记 01", section 2.2:
  * requests with a common cached prefix hold the same blocks).  Single-token
  * decode segments whose leading full partitions list the same block ids are
- * grouped, wherever they sit in the batch (calls of at most 1024 segments),
+ * grouped, wherever they sit among the call's first 1024 segments,
  * and a group reads each shared partition once for all its members instead
  * of once per member.  0 = automatic (the default:
  * min(8, 32 / G) members), 1 = no grouping, 2..8 = at most that many (never

@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   // wave per segment spreads its query tiles over the lanes
   __shared__ int pl_seg[1024], pl_n[1024], pl_len[1024], pl_c0[1024];
   __shared__ int pl_count;
-  // shared-prefix grouping of a batch of at most 1024 segments: a 2048-slot
+  // shared-prefix grouping of the first 1024 segments: a 2048-slot
   // hash set of first table entries (its storage then holds the sort keys), per segment its
   // length and covered partitions, per sorted position its segment, length,
   // link and group scratch
@@ -191,8 +191,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   SegInfo si0{0, 0, 0, false};
   int cov = 0;       // leading partitions of the thread's segment that group items cover
   int n_group = 0;
-  const bool grouping = one_chunk && p.group_max >= 2;
-  if (one_chunk) si0 = seg_info(p, threadIdx.x);
+  // (the first 1024 segments of a larger batch are grouped among themselves)
+  const bool grouping = p.group_max >= 2;
+  si0 = seg_info(p, threadIdx.x);
   if (grouping) {
     const int s = threadIdx.x;
     const bool elig0 = si0.ok && si0.n == 1 && si0.L > p.part_tokens;
@@ -227,7 +228,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       // Thread s holds position s; its partner s ^ j is in the same wave for
       // j < 64 (exchange by lane shuffle), else in LDS.
       int nsort = 2;
-      while (nsort < p.num_seqs) nsort <<= 1;
+      while (nsort < min(p.num_seqs, 1024)) nsort <<= 1;
       __syncthreads();   // the hash set's storage becomes the key array
       uint32_t key = (h << 10) | (uint32_t)s;
       for (int k = 2; k <= nsort; k <<= 1) {
@@ -344,7 +345,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   int full_base = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
-    const SegInfo si = base == 0 && one_chunk ? si0 : seg_info(p, s);
+    const SegInfo si = base == 0 ? si0 : seg_info(p, s);
     if (base == 0) first = si;
     const int cov_s = base == 0 ? cov : 0;
     int nd = 0, np = 0, nr = 0, nfull = 0;

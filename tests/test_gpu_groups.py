@@ -28,19 +28,21 @@ from workloads.synth import build
 pytestmark = pytest.mark.gpu
 
 
-def _expected(wl, part, members):
+def _expected(wl, part, members, limit=1024):
     """(group items, ordinary decode items) of the grouping rule: the
     segments with one new token, more than one partition and a valid first
     block id, sorted by (first block id, index); neighbours in that order
     link while their leading full partitions start with the same block id;
     runs of links are cut into groups of `members`, and a group of two or
-    more covers the partitions every neighbouring pair in it links.  (The
-    decode kernel then compares each grouped partition's ids whole.)"""
+    more covers the partitions every neighbouring pair in it links.  Only
+    the first `limit` segments are grouped.  (The decode kernel then compares
+    each grouped partition's ids whole.)"""
     cu, lens, tables = wl.cu_seqlens_q, wl.seq_lens, wl.block_tables
     n = np.diff(cu)
     s_count = len(lens)
     npb = part // 16
-    order = sorted((s for s in range(s_count) if n[s] == 1 and lens[s] > part and tables[s, 0] >= 0),
+    order = sorted((s for s in range(min(s_count, limit))
+                    if n[s] == 1 and lens[s] > part and tables[s, 0] >= 0),
                    key=lambda s: (int(tables[s, 0]), s))
     link = [0] * len(order)
     for r in range(1, len(order)):
@@ -126,6 +128,10 @@ CASES = {
     # sharers interleaved with other requests (every third segment shares)
     "interleaved": (lambda: build("interleaved", 4, 32, 8, 128, [(1, 1100 + 29 * i) for i in range(30)],
                                   shared_prefix=1024, shared_requests=tuple(range(0, 30, 3))), 256, None),
+    # 1100 segments: every fifth shares, on both sides of segment 1024 (only
+    # the first 1024 segments are grouped)
+    "big_batch": (lambda: build("big_batch", 4, 8, 2, 64, [(1, 140 + (37 * i) % 160) for i in range(1100)],
+                                shared_prefix=128, shared_requests=tuple(range(0, 1100, 5))), 64, None),
     # a shared prefix of 20 partitions: the plan compares 8 per round
     "long_prefix": (lambda: build("long_prefix", 2, 32, 8, 128, [(1, 2600 + 41 * i) for i in range(10)],
                                   shared_prefix=2560, shared_requests=tuple(range(10))), 128, None),
