@@ -181,8 +181,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   // than one partition whose leading full partitions start with the same
   // block ids (a cached prefix the block manager shares, "vLLM 学习笔记 01",
   // section 2.2) are grouped whatever their order in the batch: the
-  // eligible segments are sorted by (first table entry, index), neighbours
-  // in that order that share leading partitions form runs, each run is cut
+  // eligible segments are sorted so that equal first table entries are
+  // adjacent, each in index order; neighbours in that order that share
+  // leading partitions form runs, each run is cut
   // into groups of at most group_max members, and a group reads each
   // partition that all its members share once, for all of them (one group
   // item per partition).  Those partitions leave the members' own item
@@ -224,9 +225,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     // first entry together, in index order
     if (__syncthreads_or(dup)) {
       // bitonic sort of (slot, index) over the first nsort positions (a
-      // power of two >= the segment count; ineligible segments sort last).
-      // Thread s holds position s; its partner s ^ j is in the same wave for
-      // j < 64 (exchange by lane shuffle), else in LDS.
+      // power of two >= the number of segments, at most 1024; ineligible
+      // segments sort last).  Thread s holds position s; its partner s ^ j
+      // is in the same wave for j < 64 (exchanged by DPP, swizzle or lane
+      // permute), else it is read from LDS.
       int nsort = 2;
       while (nsort < min(p.num_seqs, 1024)) nsort <<= 1;
       __syncthreads();   // the hash set's storage becomes the key array
