@@ -74,9 +74,15 @@ int paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping,
                    int32_t head_dim, int64_t num_blocks, int64_t k_token_stride,
                    int64_t v_token_stride, hipStream_t stream);
 
-/* Workspace bytes paged_attention needs for these shape bounds (a pure
- * function of its arguments).  max_blocks_per_seq bounds every seq_len as
- * max_blocks_per_seq * 16; num_tokens bounds every segment's new tokens. */
+/* Workspace bytes paged_attention needs for these shape bounds.
+ * max_blocks_per_seq bounds every seq_len as max_blocks_per_seq * 16;
+ * num_tokens bounds every segment's new tokens.  num_kv_heads is needed
+ * because the decode partition size is chosen from the number of
+ * (segment, partition, KV head) work items, and the partials the workspace
+ * holds scale with the number of partitions.  The result depends on these
+ * arguments and on the calling thread's paged_attention_set_partition_tokens
+ * setting only (0 by default); a call made on the same thread with the same
+ * arguments and setting is satisfied by it.  Returns 0 for negative sizes. */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens,
                                       int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t head_dim, int32_t max_blocks_per_seq);
@@ -161,7 +167,10 @@ int paged_attention_device_status(const void* workspace, uint32_t* status,
 /* Tokens per decode partition: 0 = automatic (the default), otherwise a
  * multiple of 32 in [32, 1024].  A tuning knob for measurements; it changes
  * only the split of long decode contexts, not the result beyond rounding.
- * Process-wide; returns PAGED_EINVAL for other values. */
+ * It applies to the later paged_attention and paged_attention_workspace_size
+ * calls of the calling thread only (other threads keep their own setting; a
+ * smaller partition needs a larger workspace, so size the workspace after
+ * setting it).  Returns PAGED_EINVAL for other values. */
 int paged_attention_set_partition_tokens(int32_t tokens);
 
 /* Most members of a shared-prefix group ("vLLM 学习笔记 01", section 2.2:
@@ -172,7 +181,8 @@ int paged_attention_set_partition_tokens(int32_t tokens);
  * of once per member.  0 = automatic (the default:
  * min(8, 32 / G) members), 1 = no grouping, 2..8 = at most that many (never
  * more than 32 / G).  Results are bitwise the same either way; a knob for
- * measurements.  Process-wide; returns PAGED_EINVAL for other values. */
+ * measurements.  It applies to the later calls of the calling thread only;
+ * returns PAGED_EINVAL for other values. */
 int paged_attention_set_group_members(int32_t members);
 
 /* Measurement hook: when `count` is 5, every later paged_attention call on

@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -27,8 +26,10 @@ thread_local bool g_stage_on = false;
 hipError_t stage(int i, hipStream_t stream) {
   return g_stage_on && g_stage_events[i] ? hipEventRecord(g_stage_events[i], stream) : hipSuccess;
 }
-std::atomic<int32_t> g_part_tokens{0};
-std::atomic<int32_t> g_group_members{0};   // 0: automatic, 1: no shared-prefix groups
+// Tuning knobs of the calling thread (set by the paged_attention_set_* calls):
+// one thread's measurement setting never changes another caller's work split.
+thread_local int32_t g_part_tokens = 0;     // 0: automatic
+thread_local int32_t g_group_members = 0;   // 0: automatic, 1: no shared-prefix groups
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -57,7 +58,7 @@ int32_t max_decode_tokens(int32_t group) { return std::min(8, 32 / std::max(1, g
 // fill at most two 16-row column tiles of the decode kernel.
 int32_t group_members(int32_t group) {
   const int32_t cap = std::min(8, 32 / std::max(1, group));
-  const int32_t forced = g_group_members.load();
+  const int32_t forced = g_group_members;
   return forced > 0 ? std::min(cap, forced) : cap;
 }
 
@@ -67,7 +68,7 @@ int32_t group_members(int32_t group) {
 // so the dynamic queue balances the tail); long partitions keep the merge's
 // extra traffic, about G * (D + 2) * 8 bytes per partition, under 2 %.
 int32_t partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks) {
-  const int32_t forced = g_part_tokens.load();
+  const int32_t forced = g_part_tokens;
   if (forced > 0) return forced;
   const int64_t max_len = (int64_t)max_blocks * kBlock;
   for (int32_t p : {1024, 512, 256, 128}) {
@@ -233,7 +234,8 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
     return fail(PAGED_EINVAL, "paged_attention: scale must be finite");
   const Layout l = layout(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                           max_blocks_per_seq);
-  // the plan kernel counts prefill items in 20 bits
+  // the plan kernel sums up to 1024 per-segment item counts of at most
+  // prefill_cap + 1 each in 32-bit integers
   if (l.decode_cap > INT32_MAX / 64 || l.prefill_cap >= (1 << 20) || l.rows_cap > INT32_MAX / 64)
     return fail(PAGED_EINVAL, "paged_attention: too many work items");
   if (workspace_bytes < l.total)
@@ -421,14 +423,14 @@ int paged_attention_device_status(const void* workspace, uint32_t* status, hipSt
 int paged_attention_set_partition_tokens(int32_t tokens) {
   if (tokens != 0 && (tokens < 32 || tokens > 1024 || tokens % 32))
     return fail(PAGED_EINVAL, "partition tokens must be 0 or a multiple of 32 in [32, 1024]");
-  g_part_tokens.store(tokens);
+  g_part_tokens = tokens;
   return PAGED_OK;
 }
 
 int paged_attention_set_group_members(int32_t members) {
   if (members < 0 || members > 8)
     return fail(PAGED_EINVAL, "group members must be in [0, 8] (0: automatic, 1: off)");
-  g_group_members.store(members);
+  g_group_members = members;
   return PAGED_OK;
 }
 

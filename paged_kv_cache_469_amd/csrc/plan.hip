@@ -58,6 +58,48 @@ __device__ int block_exclusive_scan(int v, int* scratch, int* total) {
   return res;
 }
 
+// Exclusive prefix sums of N values at once over the 1024 threads of the
+// block, with one set of barriers for all of them: v[i] becomes the thread's
+// offset of value i, tot[i] the block total.  scratch holds 17 * N ints.
+template <int N>
+__device__ void block_exclusive_scan_n(int (&v)[N], int (*scratch)[N], int (&tot)[N]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = v[i];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int y = __shfl_up(x[i], off);
+      if (lane >= off) x[i] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) scratch[wave][i] = x[i];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < N) {
+    const int i = threadIdx.x;
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int t = scratch[w][i];
+      scratch[w][i] = run;
+      run += t;
+    }
+    scratch[16][i] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    tot[i] = scratch[16][i];
+    v[i] = scratch[wave][i] + x[i] - v[i];
+  }
+  __syncthreads();
+}
+
 // Inclusive maximum over the 1024 threads of the block.
 __device__ int block_inclusive_max(int v, int* scratch) {
   const int lane = threadIdx.x & 63;
@@ -155,6 +197,7 @@ constexpr int kDecodeBuckets = 1024 / 32 + 2;
 
 __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   __shared__ int scratch[17];
+  __shared__ int scan5[17][5];
   __shared__ int hist[kCostBuckets];
   __shared__ int dhist[kDecodeBuckets];
   // prefill segments of a batch of at most 1024 segments, listed so that one
@@ -336,7 +379,13 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   }
 
   // pass 1: decode items and partial rows in segment order; prefill item
-  // count and cost histogram
+  // count (and, for a batch of at most 1024 segments, the list of prefill
+  // segments).  Well-formed segments do not overlap, so their prefill items
+  // number at most prefill_cap (num_tokens / 32 + num_seqs); each count is
+  // capped at prefill_cap + 1 before the scan and the running total
+  // saturates there, so overlapping (malformed) segments can neither
+  // overflow a sum nor place a segment past the list: such a batch is
+  // flagged and its prefill items are dropped.
   int dec_base = 0;
   int row_base = 0;
   int pre_total = 0;
@@ -345,6 +394,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   int first_ofull = 0;              // and the place of its first full decode partition
   int first_tot_f = 0;              // and the first chunk's full decode partitions in all
   int full_base = 0;
+  if (threadIdx.x == 0) pl_count = 0;
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + (int)threadIdx.x;
     const SegInfo si = base == 0 ? si0 : seg_info(p, s);
@@ -361,33 +411,30 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       if (parts * p.part_tokens > si.L)
         atomicAdd(&dhist[decode_bucket(si.L - (parts - 1) * p.part_tokens, p.part_tokens)], 1);
     } else if (si.ok && si.n > p.max_decode_n) {
-      np = (si.n + p.query_tile - 1) / p.query_tile;
-      if (!one_chunk)
-        for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
+      np = min((si.n + p.query_tile - 1) / p.query_tile, p.prefill_cap + 1);
     }
-    int tot_d, tot_p, tot_r, tot_f;
-    block_exclusive_scan(nd, scratch, &tot_d);
-    const int ofull = full_base + block_exclusive_scan(nfull, scratch, &tot_f);
+    // offsets and totals of: decode items, full decode partitions, prefill
+    // items, partial rows, prefill segments
+    int sc[5] = {nd, nfull, np, nr, np > 0 ? 1 : 0};
+    int tot[5];
+    block_exclusive_scan_n<5>(sc, scan5, tot);
+    const int ofull = full_base + sc[1];
     if (base == 0) {
       first_ofull = ofull;
-      first_tot_f = tot_f;
+      first_tot_f = tot[1];
     }
-    full_base += tot_f;
-    // one scan counts the prefill items (low 20 bits: fewer than 2^20 per
-    // call) and places the prefill segments in the list (bits 20 and up)
-    const int packed = block_exclusive_scan(np + (np > 0 ? 1 << 20 : 0), scratch, &tot_p);
+    full_base += tot[1];
     if (one_chunk) {
       if (np > 0) {
-        const int k = packed >> 20;
+        const int k = sc[4];   // < 1024: the thread's place among the chunk's segments
         pl_seg[k] = s;
         pl_n[k] = si.n;
         pl_len[k] = si.L;
         pl_c0[k] = si.c0;
       }
-      if (threadIdx.x == 0) pl_count = tot_p >> 20;
+      if (threadIdx.x == 0) pl_count = tot[4];
     }
-    tot_p &= (1 << 20) - 1;
-    const int orow = row_base + block_exclusive_scan(nr, scratch, &tot_r);
+    const int orow = row_base + sc[3];
     if (s < p.num_seqs) {
       // rows past the capacity (only possible with overlapping segments):
       // the segment is skipped by the decode kernels and flagged
@@ -395,20 +442,34 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       p.seg_row[s] = fits ? orow : -1;
       if (nr > 0 && !fits) status |= 1u;
     }
-    row_base += tot_r;
-    dec_base += tot_d;
-    pre_total += tot_p;
+    row_base += tot[3];
+    dec_base += tot[0];
+    pre_total = min(pre_total + tot[2], p.prefill_cap + 1);
   }
-  if (pre_total > p.prefill_cap) status |= 1u;
   // overlapping segments (only possible when some segment is malformed)
-  // could overflow the lists: items past the capacity are dropped and flagged
+  // could overflow the lists: decode items past the capacity are dropped,
+  // and so are all prefill items when they do not fit; both are flagged
+  if (pre_total > p.prefill_cap) {
+    status |= 1u;
+    pre_total = 0;
+  }
   if (dec_base > p.decode_cap) status |= 1u;
   __syncthreads();
-  if (one_chunk && pl_count > 0) {   // pass 1b: the cost histogram, one wave per prefill segment
+  if (one_chunk && pre_total > 0) {   // pass 1b: the cost histogram, one wave per prefill segment
     for (int k = wave; k < pl_count; k += 16) {
       const int n = pl_n[k], L = pl_len[k];
       const int np = (n + p.query_tile - 1) / p.query_tile;
       for (int qt = lane; qt < np; qt += 64) atomicAdd(&hist[cost_key(n, L, qt, p.query_tile)], 1);
+    }
+    __syncthreads();
+  } else if (pre_total > 0) {   // more than 1024 segments: one thread per segment
+    for (int base = 0; base < p.num_seqs; base += 1024) {
+      const int s = base + (int)threadIdx.x;
+      const SegInfo si = base == 0 ? first : seg_info(p, s);
+      if (si.ok && si.n > p.max_decode_n) {
+        const int np = (si.n + p.query_tile - 1) / p.query_tile;
+        for (int qt = 0; qt < np; ++qt) atomicAdd(&hist[cost_key(si.n, si.L, qt, p.query_tile)], 1);
+      }
     }
     __syncthreads();
   }

@@ -43,7 +43,10 @@ def test_reduced_full_check(name, kw):
     assert st.status() == 0
 
 
-@pytest.mark.parametrize("name,kw", REDUCED[1:4], ids=["decode", "prefill", "cb"])
+SHARP = [REDUCED[0], REDUCED[1], REDUCED[2], REDUCED[3], REDUCED[5]]
+
+
+@pytest.mark.parametrize("name,kw", SHARP, ids=["tiny", "decode", "prefill", "cb", "long70b"])
 def test_sharpened_queries(name, kw):
     # q x 4: logits with std 4, outputs O(0.1-1); correctness only
     wl = workloads.make(name, **kw)
@@ -251,17 +254,59 @@ def test_bad_metadata_is_skipped_and_flagged():
         pkv.paged_validate(dup, None, None, None, 0, wl.num_blocks)
 
 
+def test_overlapping_segments_are_dropped_and_flagged():
+    # cu_seqlens_q = [0, T, 0, T, ..., T - 1, T]: the even segments each claim
+    # all T rows (malformed: the odd ones run backwards), so their prefill
+    # items (T / 32 each at G = 8) add up to far more than the list holds
+    # (and past 2^20).  The plan must flag the batch and drop every prefill
+    # item without writing outside its lists; the last segment, a well-formed
+    # single-token decode, is still computed.
+    t, hq, hkv, d = 1 << 17, 8, 1, 64
+    s_total = 1024
+    w = t // 16
+    nb = w + 8
+    log(f"case overlapping segments: S={s_total} T={t}")
+    cu = np.zeros(s_total + 1, dtype=np.int32)
+    cu[1:-1] = np.where(np.arange(1, s_total) % 2 == 1, t, 0)
+    cu[-2], cu[-1] = t - 1, t
+    lens = np.full(s_total, t, dtype=np.int32)
+    lens[-1] = 100
+    bt = np.tile(np.arange(w, dtype=np.int32), (s_total, 1))
+    rng = np.random.default_rng([469, 54])
+
+    def normal_bf16(shape):
+        x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+        return x.view(torch.int16).numpy().view(np.uint16)
+
+    k, v = normal_bf16((100, hkv, d)), normal_bf16((100, hkv, d))
+    pool = torch.zeros((nb, 2, 16, hkv, d), dtype=torch.bfloat16, device="cuda")
+    pkv.paged_kv_write(up(k), up(v), up(np.arange(100, dtype=np.int32)), pool)
+    q_host = normal_bf16((t, hq, d))
+    out = torch.full((t, hq, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(pkv.paged_attention_workspace_size(s_total, t, hq, hkv, d, w),
+                     dtype=torch.uint8, device="cuda")
+    pkv.paged_attention(up(q_host), pool, up(bt), up(cu), up(lens), 0.125, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert pkv.paged_attention_device_status(ws) & pkv.STATUS_BAD_SEGMENT
+    got = down_u16(out)
+    sentinel = np.full((hq, d), 0x40E0, dtype=np.uint16)   # bf16 7.0
+    assert (got[:t - 1] == sentinel).all(), "a dropped prefill item wrote output rows"
+    ref = paged.attend_dense(bf16.to_f64(q_host[t - 1:t]), bf16.to_f64(k), bf16.to_f64(v),
+                             0.125, 99)
+    check_close(got[t - 1:t], ref, "decode segment beside overlapping ones")
+
+
 # ------------------------------------------------------------------ full size
 
 def _full_sampled(wl, sample_segments, rows_per_segment=None, pool_blocks=None, fill_others=False,
-                  ungrouped_equal=False):
+                  ungrouped_equal=False, all_rows=()):
     """Full-size workload.  Each request's K/V is written with one
     paged_kv_write call over all its positions (the step's write order is
     covered by the reduced cases).  With ``fill_others`` only the sampled
     segments' values come from the host generator; the others are drawn on
     the GPU (seeded) and are not compared.  With ``ungrouped_equal`` the step
     is run again without shared-prefix groups and the whole output must be
-    bitwise the same."""
+    bitwise the same.  Segments in ``all_rows`` are compared on every row."""
     torch.cuda.empty_cache()
     hkv, d = wl.num_kv_heads, wl.head_dim
     nb = wl.num_blocks if pool_blocks is None else pool_blocks
@@ -307,8 +352,10 @@ def _full_sampled(wl, sample_segments, rows_per_segment=None, pool_blocks=None, 
         gv = got[:, 1].reshape(-1, hkv, d)[:length]
         rk, rv = wl.request_kv(s)
         assert np.array_equal(gk, rk) and np.array_equal(gv, rv), f"segment {s} blocks"
-    refs = oracle_rows(wl, q_host, segments=sorted(sample), rows_per_segment=rows_per_segment,
+    full = set(int(s) for s in all_rows)
+    refs = oracle_rows(wl, q_host, segments=sorted(sample - full), rows_per_segment=rows_per_segment,
                        rng=np.random.default_rng(1))
+    refs.update(oracle_rows(wl, q_host, segments=sorted(full)))
     got = down_u16(out)
     rows = np.concatenate([r for r, _ in refs.values()])
     ref = np.concatenate([x for _, x in refs.values()])
@@ -326,8 +373,11 @@ def test_full_decode_8b():
 def test_full_prefill_8b():
     wl = workloads.make("prefill_8b")
     log(f"case full prefill_8b: T={wl.num_tokens}")
-    got, ref = _full_sampled(wl, [0, 5, 9, 15], rows_per_segment=24)
-    check_close(got, ref, "prefill_8b full (4 segments x 26 rows)")
+    longest = int(np.argmax(wl.new_tokens))
+    sample = sorted({0, 5, 9, 15, longest})
+    got, ref = _full_sampled(wl, sample, rows_per_segment=24, all_rows=[longest])
+    check_close(got, ref, f"prefill_8b full (segments {sample} x 26 rows, all "
+                          f"{int(wl.new_tokens[longest])} rows of the longest, {longest})")
 
 
 def test_full_cb_step_8b():
@@ -347,8 +397,14 @@ def test_full_long_decode_70b():
     wl = workloads.make("long_decode_70b", num_blocks=nb)
     log(f"case full long_decode_70b: pool {nb} blocks ({nb * 16} tokens), "
         f"KV {wl.kv_bytes_logical() / 1e9:.1f} GB")
-    got, ref = _full_sampled(wl, [3, 40], pool_blocks=nb, fill_others=True)
-    check_close(got, ref, "long_decode_70b full (2 sampled requests)")
+    # the longest request has more than 64 partitions of 1024 keys, so its
+    # merge takes the second pass of the lanes over the partitions
+    longest = int(np.argmax(wl.seq_lens))
+    assert wl.seq_lens[longest] > 64 * 1024
+    sample = sorted({3, 40, longest})
+    got, ref = _full_sampled(wl, sample, pool_blocks=nb, fill_others=True)
+    check_close(got, ref, f"long_decode_70b full (requests {sample}; longest L = "
+                          f"{int(wl.seq_lens[longest])})")
 
 
 def test_full_spec_verify_8b():
