@@ -123,6 +123,34 @@ int paged_attention(const void* q, const void* kv_cache,
                     int32_t max_blocks_per_seq, int64_t q_token_stride,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* paged_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and kernels as
+ * paged_attention minus the workspace: its scratch (work lists, decode
+ * partials, the status word) is an array of PAGED_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every GPU it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, no hipFree, no allocating
+ * library routine); on its first call on a device it looks up that device's
+ * array (hipGetSymbolAddress), with the device current.
+ * Limits and errors: PAGED_EINVAL, with no work enqueued, when
+ * paged_attention_workspace_size(num_seqs, num_tokens, num_q_heads,
+ * num_kv_heads, head_dim, max_blocks_per_seq) on the calling thread exceeds
+ * PAGED_NOALLOC_SCRATCH_BYTES (use paged_attention with a workspace then);
+ * otherwise as paged_attention.  Every call on one GPU uses the same array
+ * and leaves its contents behind (the plan kernel rewrites what must start
+ * at zero, so nothing needs clearing): two calls that overlap on one GPU --
+ * on different streams, or from threads that do not order their streams --
+ * race and give undefined results.  Order them on one stream.  The status
+ * word of skipped metadata is not exposed; paged_validate checks metadata. */
+#define PAGED_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int paged_attention_noalloc(const void* q, const void* kv_cache,
+                            const int32_t* block_tables, const int32_t* cu_seqlens_q,
+                            const int32_t* seq_lens, float scale, void* out,
+                            int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                            int32_t max_blocks_per_seq, int64_t q_token_stride,
+                            hipStream_t stream);
+
 /* Metadata of a steady-state decode step, on the device ([NOTES01] sections
  * 1.4 and 1.6): every one of the num_seqs segments gains one new token at
  * position L = seq_lens[s] (its current length).  In place on `stream`:

@@ -12,7 +12,9 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PagedError,
     lib,
+    NOALLOC_SCRATCH_BYTES,
     paged_attention,
+    paged_attention_noalloc,
     paged_attention_device_status,
     paged_attention_set_partition_tokens,
     paged_attention_set_group_members,

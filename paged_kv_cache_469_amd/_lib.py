@@ -25,6 +25,8 @@ _SIGS = {
     "paged_attention": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_sz,
                                  _c_p]),
+    "paged_attention_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_f, _c_p, _c_i32, _c_i32,
+                                         _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i64, _c_p]),
     "paged_validate": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i64,
                                 _c_i32, _c_p]),
     "paged_attention_device_status": (_c_i32, [_c_p, ctypes.POINTER(ctypes.c_uint32), _c_p]),
@@ -159,6 +161,42 @@ def paged_attention(q, kv_cache, block_tables, cu_seqlens_q, seq_lens, scale, ou
                                  cu_seqlens_q.data_ptr(), seq_lens.data_ptr(), float(scale),
                                  out.data_ptr(), s, t, hq, hkv, d, nb, w, q.stride(0),
                                  workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PAGED_NOALLOC_SCRATCH_BYTES of include/paged_attn.h
+
+
+def paged_attention_noalloc(q, kv_cache, block_tables, cu_seqlens_q, seq_lens, scale, out,
+                            stream=None):
+    """paged_attention over the library's own per-GPU scratch: no workspace,
+    nothing allocated (``out`` must be given).  Calls that overlap on one GPU
+    race; order them on one stream."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 5)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need(out, "out", torch.bfloat16, 3)
+    nb, two, bs, hkv, d = kv_cache.shape
+    if two != 2 or bs != BLOCK or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_blocks, 2, 16, Hkv, D] tensor")
+    t, hq, dq = q.shape
+    if dq != d or q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must be [T, Hq, D] with contiguous heads")
+    s = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (s + 1,) or block_tables.shape[0] != s:
+        raise ValueError("cu_seqlens_q must be [S+1] and block_tables [S, W]")
+    for x, nm in ((block_tables, "block_tables"), (cu_seqlens_q, "cu_seqlens_q"),
+                  (seq_lens, "seq_lens")):
+        if not x.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if out.shape != (t, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T, Hq, D] tensor")
+    _check(lib().paged_attention_noalloc(q.data_ptr(), kv_cache.data_ptr(), block_tables.data_ptr(),
+                                         cu_seqlens_q.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                         out.data_ptr(), s, t, hq, hkv, d, nb,
+                                         block_tables.shape[1], q.stride(0), _stream(stream)))
     return out
 
 

@@ -9,8 +9,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
-#include <string>
-#include <vector>
 
 #include "../../include/paged_attn.h"
 #include "kernels.hpp"
@@ -19,7 +17,9 @@ using namespace pkv;
 
 namespace {
 
-thread_local std::string g_last_error;
+// Message of the last failing call on this thread (a fixed buffer: setting it
+// allocates nothing).
+thread_local char g_last_error[512] = "";
 thread_local hipEvent_t g_stage_events[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
 thread_local bool g_stage_on = false;
 
@@ -32,12 +32,10 @@ thread_local int32_t g_part_tokens = 0;     // 0: automatic
 thread_local int32_t g_group_members = 0;   // 0: automatic, 1: no shared-prefix groups
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
@@ -124,15 +122,16 @@ struct DeviceInfo {
   int prefill_wg[2] = {0, 0};
 };
 
+constexpr int kMaxDevices = 64;
 std::mutex g_dev_mu;
-std::vector<DeviceInfo> g_dev;
+DeviceInfo g_dev[kMaxDevices];   // filled on the first call on each device
 
 hipError_t device_info(DeviceInfo& out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_dev_mu);
-  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
   DeviceInfo& d = g_dev[dev];
   if (d.cus == 0) {
     int cus = 0;
@@ -209,41 +208,49 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_tokens, int3
       .total;
 }
 
-int paged_attention(const void* q, const void* kv_cache, const int32_t* block_tables,
-                    const int32_t* cu_seqlens_q, const int32_t* seq_lens, float scale, void* out,
-                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                    int32_t max_blocks_per_seq, int64_t q_token_stride, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Both attention entry points: argument checks, plan, decode, merge and
+// prefill launches over the given workspace (`who` names the entry point in
+// messages).
+int attention_impl(const char* who, const void* q, const void* kv_cache,
+                   const int32_t* block_tables, const int32_t* cu_seqlens_q,
+                   const int32_t* seq_lens, float scale, void* out, int32_t num_seqs,
+                   int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int64_t num_blocks, int32_t max_blocks_per_seq,
+                   int64_t q_token_stride, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
   int code = 0;
   if (num_seqs < 0 || num_tokens < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
-    return fail(PAGED_EINVAL, "paged_attention: negative size");
+    return fail(PAGED_EINVAL, "%s: negative size", who);
   if (!supported_dims(num_q_heads, num_kv_heads, head_dim, &code)) return code;
   if (num_seqs == 0 || num_tokens == 0) return PAGED_OK;
   if (!q || !kv_cache || !block_tables || !cu_seqlens_q || !seq_lens || !out || !workspace)
-    return fail(PAGED_EINVAL, "paged_attention: null pointer");
+    return fail(PAGED_EINVAL, "%s: null pointer", who);
   if (q_token_stride < (int64_t)num_q_heads * head_dim || q_token_stride % 8)
-    return fail(PAGED_EINVAL, "paged_attention: q_token_stride must be >= Hq * D and a multiple of 8");
+    return fail(PAGED_EINVAL, "%s: q_token_stride must be >= Hq * D and a multiple of 8", who);
   if ((uintptr_t)q % 16 || (uintptr_t)kv_cache % 16 || (uintptr_t)out % 16 ||
       (uintptr_t)workspace % 256)
-    return fail(PAGED_EINVAL, "paged_attention: q/kv_cache/out need 16-byte and workspace "
-                              "256-byte alignment");
+    return fail(PAGED_EINVAL, "%s: q/kv_cache/out need 16-byte and workspace "
+                              "256-byte alignment", who);
   if ((int64_t)max_blocks_per_seq * kBlock > INT32_MAX / 2)
-    return fail(PAGED_EINVAL, "paged_attention: max_blocks_per_seq too large");
+    return fail(PAGED_EINVAL, "%s: max_blocks_per_seq too large", who);
   if (!(scale == scale) || std::isinf(scale))
-    return fail(PAGED_EINVAL, "paged_attention: scale must be finite");
+    return fail(PAGED_EINVAL, "%s: scale must be finite", who);
   const Layout l = layout(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
                           max_blocks_per_seq);
   // the plan kernel sums up to 1024 per-segment item counts of at most
   // prefill_cap + 1 each in 32-bit integers
   if (l.decode_cap > INT32_MAX / 64 || l.prefill_cap >= (1 << 20) || l.rows_cap > INT32_MAX / 64)
-    return fail(PAGED_EINVAL, "paged_attention: too many work items");
+    return fail(PAGED_EINVAL, "%s: too many work items", who);
   if (workspace_bytes < l.total)
-    return fail(PAGED_EINVAL, "paged_attention: workspace of %zu bytes, %zu needed",
+    return fail(PAGED_EINVAL, "%s: workspace of %zu bytes, %zu needed", who,
                 workspace_bytes, l.total);
   DeviceInfo dev;
   hipError_t e = device_info(dev);
-  if (e != hipSuccess) return fail_hip(e, "paged_attention device query");
+  if (e != hipSuccess) return fail_hip(e, "device query");
 
   char* ws = static_cast<char*>(workspace);
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
@@ -277,7 +284,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   e = stage(0, stream);
   if (e == hipSuccess) e = launch_plan(pp, stream);
   if (e == hipSuccess) e = stage(1, stream);
-  if (e != hipSuccess) return fail_hip(e, "paged_attention plan launch");
+  if (e != hipSuccess) return fail_hip(e, "plan launch");
 
   const int di = head_dim == 128 ? 1 : 0;
   DecodeParams dp{};
@@ -309,7 +316,7 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   if (e == hipSuccess) e = stage(2, stream);
   if (e == hipSuccess) e = launch_decode_merge(dp, head_dim, num_seqs, num_tokens, stream);
   if (e == hipSuccess) e = stage(3, stream);
-  if (e != hipSuccess) return fail_hip(e, "paged_attention decode launch");
+  if (e != hipSuccess) return fail_hip(e, "decode launch");
 
   PrefillParams fp{};
   fp.q = dp.q;
@@ -340,8 +347,81 @@ int paged_attention(const void* q, const void* kv_cache, const int32_t* block_ta
   prefill_grid = std::max<int64_t>(fp.num_queues, prefill_grid / fp.num_queues * fp.num_queues);
   e = launch_prefill(fp, head_dim, (int)prefill_grid, stream);
   if (e == hipSuccess) e = stage(4, stream);
-  if (e != hipSuccess) return fail_hip(e, "paged_attention prefill launch");
+  if (e != hipSuccess) return fail_hip(e, "prefill launch");
   return PAGED_OK;
+}
+
+
+// Scratch of paged_attention_noalloc: one array per GPU (each device that
+// loads the library holds its own copy until the process ends).  Host code
+// never passes the array's name to a kernel: that is a host-side stand-in,
+// not a device address.  The address of each device's copy comes from
+// hipGetSymbolAddress with that device current, once, and is kept here.
+constexpr size_t kScratchBytes = PAGED_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "paged_attention_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PAGED_EINVAL, "paged_attention_noalloc: device %d beyond the %d supported", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "paged_attention_noalloc: hipGetSymbolAddress");
+    if (!p) return fail(PAGED_EHIP, "paged_attention_noalloc: no address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PAGED_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention(const void* q, const void* kv_cache, const int32_t* block_tables,
+                    const int32_t* cu_seqlens_q, const int32_t* seq_lens, float scale, void* out,
+                    int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                    int32_t max_blocks_per_seq, int64_t q_token_stride, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return attention_impl("paged_attention", q, kv_cache, block_tables, cu_seqlens_q, seq_lens,
+                        scale, out, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                        num_blocks, max_blocks_per_seq, q_token_stride, workspace,
+                        workspace_bytes, stream);
+}
+
+int paged_attention_noalloc(const void* q, const void* kv_cache, const int32_t* block_tables,
+                            const int32_t* cu_seqlens_q, const int32_t* seq_lens, float scale,
+                            void* out, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                            int32_t max_blocks_per_seq, int64_t q_token_stride,
+                            hipStream_t stream) {
+  if (num_seqs >= 0 && num_tokens >= 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 &&
+      max_blocks_per_seq >= 0) {
+    const size_t need = paged_attention_workspace_size(num_seqs, num_tokens, num_q_heads,
+                                                       num_kv_heads, head_dim, max_blocks_per_seq);
+    if (need > kScratchBytes)
+      return fail(PAGED_EINVAL,
+                  "paged_attention_noalloc: these shapes need %zu bytes of scratch, more than "
+                  "the %zu the library holds per GPU (use paged_attention with a workspace)",
+                  need, kScratchBytes);
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0 && num_tokens > 0) {
+    const int code = scratch_ptr(&ws);
+    if (code != PAGED_OK) return code;
+  }
+  return attention_impl("paged_attention_noalloc", q, kv_cache, block_tables, cu_seqlens_q,
+                        seq_lens, scale, out, num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                        head_dim, num_blocks, max_blocks_per_seq, q_token_stride, ws,
+                        kScratchBytes, stream);
 }
 
 int paged_decode_advance(int32_t* seq_lens, int32_t* cu_seqlens_q, int32_t* slot_mapping,
@@ -450,6 +530,6 @@ int paged_attention_set_stage_events(void* const* events, int32_t count) {
   return PAGED_OK;
 }
 
-const char* paged_last_error(void) { return g_last_error.c_str(); }
+const char* paged_last_error(void) { return g_last_error; }
 
 }  // extern "C"
