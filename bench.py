@@ -3,22 +3,30 @@
 
 A step is one pass of the whole path over one batch: the KV block write of
 the step's new tokens, then paged attention (device-side plan, split-context
-decode, partition merge, prefill).  Default workload: the Llama-3-8B-shaped
-decode batch (256 requests, 32 query / 8 KV heads, head_dim 128, one new
-token each over a cached context uniform in [512, 4096], blocks scattered at
-random in a pool sized to the total).  ``value`` is KV bytes attention must
-read (per request, L * 2 * Hkv * D * 2) per second of whole-step time.
+decode, partition merge, prefill).
 
-Also reported on the same line:
-* ``roofline`` for the dominant kernel (decode): algorithmic KV bytes per
-  launch / the kernel's mean duration, timed with two HIP events recorded on
-  the launch stream around that kernel only, over as many steps again as the
-  timed ones (``kernels_us`` breaks a step down with events around every
-  kernel, in a third pass);
-* ``prefill``: the prefill batch (16 prompts of 256..2048 tokens), attention
-  TFLOP/s of the prefill kernel against the bf16 dense MFMA peak;
+Default run (``--workload all``): the headline is the 70B-shaped long-context
+decode batch (64 requests, 64 query / 8 KV heads, head_dim 128, one new token
+each over a cached context uniform in [32768, 131072], blocks scattered at
+random in a pool of about 0.92 of free HBM); ``value`` is the KV bytes
+attention must read (L * 2 * Hkv * D * 2 per request) per second of
+whole-step time.  The other four workloads follow as line items under
+``items`` (the 8B-shaped decode batch, the prefill batch, the
+continuous-batching step and the tiny mixed step), each with the same fields.
+
+Per workload:
+* ``ms_per_step``: exactly ``--steps`` steps between two events (the tiny
+  mixed step: 50 times as many), and ``step_us_median`` / ``step_us_min``
+  from events around each step in a second pass;
+* ``roofline`` for the dominant kernel (decode: HBM GB/s of algorithmic KV
+  bytes; prefill: TFLOP/s of unmasked (query, key) pairs against the bf16
+  dense MFMA peak): algorithmic work per launch / the kernel's mean launch
+  duration, timed with two HIP events on the launch stream around that
+  kernel only; the continuous-batching step has both (``roofline`` for its
+  decode part, ``roofline_chunk`` for its chunk) and its lower bounds;
+* ``traffic``: HBM bytes per launch from committed counter summaries;
 * ``cpu_baseline``: the fp64 CPU oracle on a bounded sample of the same
-  decode batch (gather + attention timed; data generation not).
+  workload (gather + attention timed; data generation not).
 
 Inputs are synthetic: lengths and block placement from the seeded workload
 generators, values N(0,1) drawn on the GPU with a seeded generator.
@@ -107,57 +115,70 @@ class Setup:
                                  out=self.out, workspace=self.ws)
 
 
-def run_steps(setup, steps, warmup, dominant):
-    """Time `steps` steps; returns (ms_per_step, per-kernel mean us, mean us
-    of the `dominant` kernel).
+STAGES = ["plan", "decode", "decode_merge", "prefill"]
 
-    The whole-step time comes from the timed steps alone (nothing but the
-    calls between the two events).  The dominant kernel's time (the one the
-    roofline is reported for) comes from the same number of steps run again
-    with only the two HIP events around that kernel; the per-kernel breakdown
-    from a third such pass with events around every kernel (each record adds
-    a few microseconds between kernels, and the idle gaps slow the prefill
-    kernel that follows them by several per cent, so the roofline does not
-    use that pass)."""
+# Passes over the steps of one workload, in this order, each of the same
+# number of steps (``trace_summary`` splits a kernel trace of a bench run by
+# the same plan):
+#   timed      nothing but the calls between two events: the step time;
+#   per-step   two events around every step: median and min of a step;
+#   kernel <k> two events around kernel k only, once for each roofline kernel
+#              of the workload: its mean, median and min launch duration;
+#   stages     events around every kernel: the per-kernel breakdown (each
+#              record leaves a gap of a few microseconds between kernels, so
+#              these times are not used for the rooflines).
+# One warm-up pass of `warmup` steps comes first.
+def passes_of(dominant):
+    return ["timed", "per_step"] + [f"kernel:{k}" for k in dominant] + ["stages"]
+
+
+def run_steps(setup, steps, warmup, dominant):
+    """Runs the passes above; returns a dict of their results."""
     import torch
 
     pkv = setup.pkv
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    stage_sets = [[mk() for _ in range(5)] for _ in range(steps)]
-    write_sets = [(mk(), mk()) for _ in range(steps)]
-    for evs in stage_sets + write_sets:        # create the HIP events outside the timed region
+
+    def made(evs):                     # create the HIP events outside the timed regions
         for e in evs:
             e.record()
+        return evs
+
+    stage_sets = [made([mk() for _ in range(5)]) for _ in range(steps)]
+    write_sets = [made([mk(), mk()]) for _ in range(steps)]
+    step_sets = [made([mk(), mk()]) for _ in range(steps)]
+    dom_sets = {k: [made([mk(), mk()]) for _ in range(steps)] for k in dominant}
+    start, end = made([mk(), mk()])
     for _ in range(warmup):
         setup.step()
     torch.cuda.synchronize()
-    start, end = mk(), mk()
+    # timed: exactly `steps` steps between two events
     start.record()
     for _ in range(steps):
         setup.step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-
-    # the dominant kernel alone: events around it only
-    names = ["plan", "decode", "decode_merge", "prefill"]
-    k = names.index(dominant)
-    dom_sets = [[mk(), mk()] for _ in range(steps)]
-    for evs in dom_sets:
-        for e in evs:
-            e.record()
+    # per step
+    for a, b in step_sets:
+        a.record()
+        setup.step()
+        b.record()
     torch.cuda.synchronize()
-    for i in range(steps):
-        evs = [None] * 5
-        evs[k], evs[k + 1] = dom_sets[i]
-        pkv.paged_attention_set_stage_events(evs)
-        pkv.paged_kv_write(setup.k, setup.v, setup.slots, setup.pool)
-        pkv.paged_attention(setup.q, setup.pool, setup.bt, setup.cu, setup.lens, setup.wl.scale,
-                            out=setup.out, workspace=setup.ws)
-    torch.cuda.synchronize()
-    pkv.paged_attention_set_stage_events(None)
-    dom_us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in dom_sets]))
-
+    step_us = [1e3 * a.elapsed_time(b) for a, b in step_sets]
+    # each roofline kernel alone: events around it only
+    dom = {}
+    for k in dominant:
+        i = STAGES.index(k)
+        for evs2 in dom_sets[k]:
+            evs = [None] * 5
+            evs[i], evs[i + 1] = evs2
+            pkv.paged_attention_set_stage_events(evs)
+            setup.step()
+        torch.cuda.synchronize()
+        pkv.paged_attention_set_stage_events(None)
+        d = [1e3 * a.elapsed_time(b) for a, b in dom_sets[k]]
+        dom[k] = {"mean": float(np.mean(d)), "median": float(np.median(d)), "min": float(np.min(d))}
     # every kernel
     for i in range(steps):
         pkv.paged_attention_set_stage_events(stage_sets[i])
@@ -169,23 +190,22 @@ def run_steps(setup, steps, warmup, dominant):
     torch.cuda.synchronize()
     pkv.paged_attention_set_stage_events(None)
     us = {n: 1e3 * float(np.mean([s[i].elapsed_time(s[i + 1]) for s in stage_sets]))
-          for i, n in enumerate(names)}
+          for i, n in enumerate(STAGES)}
     us["kv_write"] = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in write_sets]))
     status = pkv.paged_attention_device_status(setup.ws)
     if status:
         raise RuntimeError(f"device status {status}: metadata rejected")
-    return ms, us, dom_us
+    return {"ms": ms, "step_us": {"median": float(np.median(step_us)), "min": float(np.min(step_us))},
+            "kernels_us": us, "dominant": dom}
 
 
-def cpu_baseline_decode(wl, sample):
-    """The fp64 oracle on `sample` requests of a decode batch: gather from a
-    host pool + attention, timed; generation and pool filling untimed."""
-    from threadpoolctl import threadpool_limits
+# ------------------------------------------------------------------ oracle beside it
 
+def _oracle_pool(wl, sel):
+    """A host pool holding the K/V of segments `sel` (their blocks renumbered
+    contiguously) and their tables: untimed set-up of a CPU baseline."""
     from oracle import paged
 
-    cores = len(os.sched_getaffinity(0))
-    sel = list(range(min(sample, wl.num_seqs)))
     hkv, d = wl.num_kv_heads, wl.head_dim
     nblk = [(int(wl.seq_lens[s]) + 15) // 16 for s in sel]
     pool = np.empty((sum(nblk), 2, 16, hkv, d), dtype=np.uint16)
@@ -198,6 +218,21 @@ def cpu_baseline_decode(wl, sample):
         pos = np.arange(length)
         paged.kv_write(k, v, (tables[i][pos // 16].astype(np.int64) * 16 + pos % 16), pool)
         c += nblk[i]
+    return pool, tables
+
+
+def cpu_baseline_decode(wl, sample):
+    """The fp64 oracle on `sample` decode requests of a batch: gather from a
+    host pool + attention, timed; generation and pool filling untimed."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+
+    cores = len(os.sched_getaffinity(0))
+    dec = [s for s in range(wl.num_seqs) if 1 <= wl.new_tokens[s] <= 8]
+    sel = dec[:sample]
+    hkv, d = wl.num_kv_heads, wl.head_dim
+    pool, tables = _oracle_pool(wl, sel)
     q = wl.q()
     cu = wl.cu_seqlens_q
     rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in sel])
@@ -210,27 +245,54 @@ def cpu_baseline_decode(wl, sample):
         dt = time.perf_counter() - t0
     kv = int(lens.astype(np.int64).sum()) * 2 * hkv * d * 2
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(sel)} of {wl.num_seqs} requests of the same batch "
+            "sample": f"{len(sel)} of {len(dec)} decode requests of the same batch "
                       f"({kv / 1e9:.3f} GB of KV), gather + fp64 attention timed: {dt:.2f} s"}
 
 
-def prefill_cpu_baseline(wl):
+def cpu_baseline_prefill(wl, seg, rows=None):
+    """The fp64 oracle on segment `seg` of a batch (all its rows, or the
+    `rows` last ones), gather from a host pool + attention timed."""
     from threadpoolctl import threadpool_limits
 
     from oracle import bf16, paged
 
     cores = len(os.sched_getaffinity(0))
-    s = int(np.argmin(wl.new_tokens))
-    n = int(wl.new_tokens[s])
-    k, v = wl.request_kv(s)
-    q = wl.q()[wl.cu_seqlens_q[s]:wl.cu_seqlens_q[s + 1]]
+    n = int(wl.new_tokens[seg])
+    length = int(wl.seq_lens[seg])
+    h = length - n
+    r = n if rows is None else min(rows, n)
+    pool, tables = _oracle_pool(wl, [seg])
+    q = wl.q()[wl.cu_seqlens_q[seg] + n - r:wl.cu_seqlens_q[seg + 1]]
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
-        paged.attend_dense(bf16.to_f64(q), bf16.to_f64(k), bf16.to_f64(v), wl.scale, 0)
+        k, v = paged.gather(pool, tables[0], length)
+        paged.attend_dense(bf16.to_f64(q), bf16.to_f64(k), bf16.to_f64(v), wl.scale, h + n - r)
         dt = time.perf_counter() - t0
-    flops = 4 * wl.head_dim * wl.num_q_heads * n * (n + 1) // 2
+    pairs = r * (h + n - r) + r * (r + 1) // 2
+    flops = 4 * wl.head_dim * wl.num_q_heads * pairs
+    what = f"all {n} rows" if r == n else f"the last {r} of its {n} rows"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"segment {s} ({n} tokens) of the prefill batch: {dt:.2f} s"}
+            "sample": f"segment {seg} ({what}, {h + n - r} keys before the first) of the same "
+                      f"batch: {flops / 1e9:.1f} GFLOP, gather + fp64 attention timed: {dt:.2f} s"}
+
+
+def cpu_baseline_step(wl, reps):
+    """The fp64 oracle on the whole step, `reps` times: time per step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+
+    cores = len(os.sched_getaffinity(0))
+    sel = list(range(wl.num_seqs))
+    pool, tables = _oracle_pool(wl, sel)
+    q = wl.q()
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            paged.attend(q, pool, tables, wl.cu_seqlens_q, wl.seq_lens, wl.scale)
+        dt = time.perf_counter() - t0
+    return {"value": 1e6 * dt / reps, "unit": "us/step", "cores": cores, "kind": "oracle",
+            "sample": f"the whole step, {reps} times (gather + fp64 attention): {dt:.2f} s"}
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -330,9 +392,9 @@ def pmc_summary(args):
         "#",
         "# Commands (from the repository root, on one MI355X):",
         f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex {args.kernel} -f csv -d <F> -o k -- "
-        f"python bench.py --workload {args.workload} --steps 3 --warmup 1 --no-prefill --no-cpu-baseline",
+        f"python bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline",
         f"#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex {args.kernel} -f csv -d <W> -o k -- "
-        f"python bench.py --workload {args.workload} --steps 3 --warmup 1 --no-prefill --no-cpu-baseline",
+        f"python bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline",
         "#   rocprofv3 --pmc FETCH_SIZE -f csv -d <CF> -o copy -- python bench.py --copy-calibration",
         "#   rocprofv3 --pmc WRITE_SIZE -f csv -d <CW> -o copy -- python bench.py --copy-calibration",
         f"#   python bench.py --pmc-summary --kernel {args.kernel} --workload {args.workload} "
@@ -354,49 +416,185 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE"]
+
+
+def mfma_summary(args):
+    """Matrix-core busy time and the shader clock of one kernel, from one
+    rocprofv3 run with --pmc of MFMA_COUNTERS and --kernel-trace (durations of
+    the same dispatches).  GRBM_GUI_ACTIVE comes summed over the XCDs (one
+    instance each), so cycles = GRBM_GUI_ACTIVE / XCDs:
+      busy  = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * CUs * 4 SIMDs)
+      clock = cycles / dispatch duration (cycles per ns = GHz)
+      executed flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (every MFMA the
+      kernel issues, masked products included), against the algorithmic
+      flops of the workload's segments on that kernel."""
+    import workloads
+
+    trace = glob.glob(os.path.join(args.trace, "*kernel_trace.csv"))[0]
+    dur = {}
+    with open(trace) as fh:
+        for r in csv.DictReader(fh):
+            if args.kernel in r["Kernel_Name"]:
+                dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    per = {}
+    for f in glob.glob(os.path.join(args.counters, "*counter_collection.csv")):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if args.kernel in r["Kernel_Name"]:
+                    per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    ids = sorted((i for i in per if i in dur and len(per[i]) == len(MFMA_COUNTERS)), key=int)
+    cus = args.cus
+    wl = workloads.make(args.workload) if args.workload != "long_decode_70b" else None
+    alg = None
+    if wl is not None:
+        _, pre, _ = _decode_split(wl)
+        alg = wl.attention_flops(segments=pre) if pre.size else 0
+    rows = []
+    for i in ids:
+        c, ns = per[i], dur[i]
+        cyc = c["GRBM_GUI_ACTIVE"] / args.xcds          # the dispatch's cycles on one XCD
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * 4)
+        ghz = cyc / ns
+        exe = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+        rows.append((i, ns / 1e3, busy, ghz, exe, c["SQ_BUSY_CYCLES"]))
+    lines = [
+        f"# Matrix-core busy time and shader clock of {args.kernel}<128>, workload {args.workload}",
+        "#",
+        "# Commands (from the repository root, on one MI355X):",
+        f"#   rocprofv3 --kernel-trace --pmc {' '.join(MFMA_COUNTERS)} --kernel-include-regex "
+        f"{args.kernel} -f csv -d <C> -o m -- python bench.py --workload {args.workload} "
+        "--steps 3 --warmup 1 --no-cpu-baseline",
+        f"#   python bench.py --mfma-summary --kernel {args.kernel} --workload {args.workload} "
+        "--counters <C> --trace <C>",
+        "#",
+        "# cycles = GRBM_GUI_ACTIVE / 8: rocprofv3 sums the counter over its 8 instances (one per",
+        "#   XCD; each counts the dispatch's cycles at the shader clock);",
+        "# busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * 256 CUs * 4 SIMDs): the share of the",
+        "#   dispatch's cycles in which an average SIMD's matrix core was busy;",
+        "# clock = cycles / duration, in GHz; the 2516.6 TFLOP/s peak assumes 2.4 GHz.  Check:",
+        "#   busy * clock * 1024 flop per SIMD-cycle * 1024 SIMDs = executed flops per second;",
+        "# executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512: the flops of every MFMA issued, masked",
+        "#   or idle products included; algorithmic = 4 * D * Hq per unmasked (query, key) pair.",
+        "#   Counter collection serialises dispatches, so durations here may differ a little",
+        "#   from the bench's own events.",
+        f"cus: {cus}",
+        f"algorithmic_flops_per_launch: {alg}",
+        "",
+        "| dispatch | us | MFMA busy | clock GHz | busy x clock x 1 PFLOP/GHz | executed TFLOP | "
+        "executed TFLOP/s | algorithmic TFLOP/s | algorithmic / executed |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for i, us, busy, ghz, exe, _ in rows:
+        a = f"{alg / (us * 1e-6) / 1e12:.0f}" if alg else "-"
+        r = f"{alg / exe:.3f}" if alg else "-"
+        lines.append(f"| {i} | {us:.1f} | {100 * busy:.1f} % | {ghz:.3f} | "
+                     f"{busy * ghz * 1024 * 1024 / 1e3:.0f} | {exe / 1e12:.4f} | "
+                     f"{exe / (us * 1e-6) / 1e12:.0f} | {a} | {r} |")
+    if rows:
+        m = lambda k: float(np.mean([x[k] for x in rows]))
+        lines += ["", f"mean_us: {m(1):.1f}", f"mean_mfma_busy: {m(2):.4f}",
+                  f"mean_clock_ghz: {m(3):.3f}",
+                  f"mean_executed_tflops_per_s: {np.mean([x[4] / (x[1] * 1e-6) / 1e12 for x in rows]):.1f}"]
+        if alg:
+            lines.append(f"mean_algorithmic_tflops_per_s: {np.mean([alg / (x[1] * 1e-6) / 1e12 for x in rows]):.1f}")
+    print("\n".join(lines))
+
+
+# The default run: the long-context decode batch as the headline, then the
+# other four workloads as line items, in this order.  Per workload: the
+# kernels whose rooflines are reported, and the step count (the tiny mixed
+# step is timed over 50 times as many steps: it takes tens of microseconds).
+DEFAULT_RUN = ["long_decode_70b", "decode_8b", "prefill_8b", "cb_step_8b", "tiny_mixed"]
+DOMINANT = {"prefill_8b": ["prefill"], "cb_step_8b": ["decode", "prefill"], "tiny_mixed": []}
+STEP_FACTOR = {"tiny_mixed": 50}
+
+
+def dominant_of(name):
+    return DOMINANT.get(name, ["decode"])
+
+
+def run_plan(workload, steps, warmup):
+    """[(workload, steps, warmup, passes)] of a bench run, in order."""
+    names = DEFAULT_RUN if workload == "all" else [workload]
+    plan = []
+    for n in names:
+        f = STEP_FACTOR.get(n, 1) if workload == "all" else 1
+        plan.append((n, steps * f, warmup * f, passes_of(dominant_of(n))))
+    return plan
+
+
 def trace_summary(args):
     """Per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench
-    command.  For the default command (decode_8b) the trace is split into its
-    two phases (decode_8b, then prefill_8b) by counting the KV-write
-    dispatches that open every step; for another --workload it is one phase."""
+    command, split into the bench's phases (workloads and passes) by counting
+    the KV-write dispatch that opens every step, in the order of run_plan."""
     path = glob.glob(os.path.join(args.trace, "*kernel_trace.csv"))[0]
     with open(path) as fh:
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
     rows = [r for r in rows if "pkv::" in r["Kernel_Name"]]
-    default = args.workload == "decode_8b"
-    wl_flag = "" if default else f" --workload {args.workload}"
-    if default:
-        n_dec = args.warmup + 3 * args.steps             # decode_8b steps (timed + two event passes)
-        phases, seen = {"decode_8b": [], "prefill_8b": []}, 0
-        for r in rows:
-            if "kv_write" in r["Kernel_Name"]:
-                seen += 1
-            phases["decode_8b" if seen <= n_dec else "prefill_8b"].append(r)
-        title = "default bench (decode_8b headline, prefill_8b line item)"
-    else:
-        phases = {args.workload: rows}
-        title = f"{args.workload}: {DESCRIPTIONS[args.workload]}"
+    plan = run_plan(args.workload, args.steps, args.warmup)
+    # phase boundaries in KV-write dispatches
+    bounds = []
+    for name, steps, warmup, passes in plan:
+        bounds.append((name, "warm-up", warmup))
+        for ps in passes:
+            bounds.append((name, ps, steps))
+    phases, bi, seen = [], -1, 0
+    for r in rows:
+        if "kv_write" in r["Kernel_Name"]:
+            if bi < 0 or seen == bounds[bi][2]:
+                bi += 1
+                seen = 0
+                phases.append((bounds[bi][0], bounds[bi][1], []))
+            seen += 1
+        phases[-1][2].append(r)
+    flag = "" if args.workload == "all" else f" --workload {args.workload}"
+    title = ("default bench (long_decode_70b headline; decode_8b, prefill_8b, cb_step_8b, "
+             "tiny_mixed line items)" if args.workload == "all"
+             else f"{args.workload}: {DESCRIPTIONS[args.workload]}")
     out = [f"# Kernel trace: {title}", "",
            "Command (from the repository root, on one MI355X):", "",
-           f"    rocprofv3 --kernel-trace --stats -f csv -d <T> -o kt -- python bench.py{wl_flag} "
+           f"    rocprofv3 --kernel-trace --stats -f csv -d <T> -o kt -- python bench.py{flag} "
            f"--steps {args.steps} --warmup {args.warmup} --no-cpu-baseline",
-           f"    python bench.py --trace-summary --trace <T>{wl_flag} --steps {args.steps} --warmup {args.warmup}",
-           "", "Durations in microseconds (end - start of each dispatch): per step one warm-up, then "
-           "three passes of the steps (timed; events around the roofline kernel; events around "
-           "every kernel).", ""]
-    for ph, rs in phases.items():
+           f"    python bench.py --trace-summary --trace <T>{flag} --steps {args.steps} "
+           f"--warmup {args.warmup}",
+           "",
+           "Durations in microseconds (end - start of each dispatch).  Per workload the bench "
+           "runs a warm-up, then passes of the same number of steps: timed (the step time), "
+           "per-step (events around each step), one pass per roofline kernel (events around "
+           "that kernel only: the pass whose times the bench line reports for it) and stages "
+           "(events around every kernel).", ""]
+
+    def table(rs):
         by = {}
         for r in rs:
-            name = r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0]
+            name = (r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+                    .split("(")[0])
             d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             by.setdefault(name, {"d": [], "r": r})["d"].append(d)
-        out += [f"### phase: {ph}", "", "| kernel | calls | avg us | min us | max us | grid (threads) | wg | vgpr | lds B |",
-                "|---|---|---|---|---|---|---|---|---|"]
+        t = ["| kernel | calls | avg us | median us | min us | max us | grid (threads) | wg | "
+             "vgpr | lds B |", "|---|---|---|---|---|---|---|---|---|---|"]
         for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1]["d"])):
             d, r = v["d"], v["r"]
-            out.append(f"| {name} | {len(d)} | {sum(d) / len(d):.1f} | {min(d):.1f} | {max(d):.1f} | "
-                       f"{r['Grid_Size_X']} | {r['Workgroup_Size_X']} | {r['VGPR_Count']} | {r['LDS_Block_Size']} |")
+            t.append(f"| {name} | {len(d)} | {np.mean(d):.1f} | {np.median(d):.1f} | {min(d):.1f} | "
+                     f"{max(d):.1f} | {r['Grid_Size_X']} | {r['Workgroup_Size_X']} | "
+                     f"{r['VGPR_Count']} | {r['LDS_Block_Size']} |")
+        return t
+
+    for name, _, _, _ in plan:
+        mine = [ph for ph in phases if ph[0] == name]
+        allrows = [r for ph in mine for r in ph[2]]
+        out += [f"## {name}", "", "All passes but the warm-up:", ""]
+        out += table([r for ph in mine if ph[1] != "warm-up" for r in ph[2]])
+        for ph in mine:
+            if ph[1].startswith("kernel:"):
+                k = ph[1].split(":", 1)[1]
+                out += ["", f"Pass `{ph[1]}` (the {k} kernel's roofline time in the bench line "
+                        f"comes from this pass's events):", ""]
+                out += table(ph[2])
         out.append("")
+        del allrows
     print("\n".join(out))
 
 
@@ -414,18 +612,98 @@ def make_workload(name):
     return workloads.make(name), None
 
 
-def measure(name, steps, warmup):
+def _decode_split(wl):
+    """(decode segments, prefill segments, algorithmic KV bytes of the decode
+    kernel: unique bytes, each shared prefix block counted once)."""
+    # segments on the split-context decode path: n * G <= 32 and n <= 8
+    max_dec = min(8, 32 // (wl.num_q_heads // wl.num_kv_heads))
+    dec = np.nonzero((wl.new_tokens >= 1) & (wl.new_tokens <= max_dec))[0]
+    pre = np.nonzero(wl.new_tokens > max_dec)[0]
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * 2
+    dec_bytes = int(wl.seq_lens[dec].astype(np.int64).sum()) * per_tok
+    if wl.shared_prefix:
+        dec_bytes = wl.kv_bytes_unique() - int(wl.seq_lens[pre].astype(np.int64).sum()) * per_tok
+    return dec, pre, dec_bytes
+
+
+def _roofline(kind, work, kernel_times, traffic_key):
+    """Roofline entry of one kernel: `work` algorithmic bytes or flops per
+    launch over its mean launch duration."""
+    us = kernel_times["mean"]
+    if kind == "decode":
+        ach = work / (us * 1e-6) / 1e9
+        return {"kernel": "decode_kernel<128>", "bound": "hbm", "achieved": ach,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "kernel_us": us,
+                "kernel_us_median": kernel_times["median"], "kernel_us_min": kernel_times["min"],
+                "algorithmic_bytes": work, "traffic": stored_traffic("decode_kernel", traffic_key)}
+    ach = work / (us * 1e-6) / 1e12
+    return {"kernel": "prefill_kernel<128>", "bound": "mfma", "achieved": ach,
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+            "kernel_us": us, "kernel_us_median": kernel_times["median"],
+            "kernel_us_min": kernel_times["min"], "algorithmic_flops": work,
+            "traffic": stored_traffic("prefill_kernel", traffic_key)}
+
+
+def bench_workload(name, steps, warmup, with_cpu, cpu_sample=None):
+    """Times one workload (set-up untimed) and returns its entry of the line."""
     import torch
 
     wl, nb = make_workload(name)
-    log(f"[bench] {name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")
+    log(f"[bench] {name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}, {steps} steps")
     st = Setup(wl, pool_blocks=nb)
-    dominant = "prefill" if name == "prefill_8b" else "decode"
-    ms, us, dom_us = run_steps(st, steps, warmup, dominant)
-    res = {"wl": wl, "ms": ms, "us": us, "dom_us": dom_us, "pool_tokens": wl.num_blocks * 16}
+    res = run_steps(st, steps, warmup, dominant_of(name))
     del st
     torch.cuda.empty_cache()
-    return res
+    ms = res["ms"]
+    dec, pre, dec_bytes = _decode_split(wl)
+    flops = wl.attention_flops()
+    pre_flops = wl.attention_flops(segments=pre) if pre.size else 0
+    kv_bytes = wl.kv_bytes_unique()
+    e = {"workload": f"{name}: {DESCRIPTIONS[name]}", "steps": steps, "warmup": warmup,
+         "ms_per_step": ms, "step_us_median": res["step_us"]["median"],
+         "step_us_min": res["step_us"]["min"],
+         "config": {"num_seqs": wl.num_seqs, "num_tokens": wl.num_tokens,
+                    "heads": [wl.num_q_heads, wl.num_kv_heads], "head_dim": wl.head_dim,
+                    "block_size": 16, "pool_blocks": wl.num_blocks, "kv_bytes": kv_bytes,
+                    "attention_flops": flops}}
+    dom = res["dominant"]
+    if name == "prefill_8b":
+        e.update(value=flops / (ms * 1e-3) / 1e12, unit="TFLOP/s")
+        e["roofline"] = _roofline("prefill", pre_flops, dom["prefill"], name)
+    elif name == "tiny_mixed":
+        e.update(value=1e3 * ms, unit="us/step")
+        e["roofline"] = None
+        e["roofline_note"] = "latency-bound step (a few kernels of a few microseconds each)"
+    else:
+        e.update(value=kv_bytes / (ms * 1e-3) / 1e9, unit="GB/s")
+        e["roofline"] = _roofline("decode", dec_bytes, dom["decode"], name)
+    if name == "cb_step_8b":
+        e["config"]["kv_bytes_logical"] = wl.kv_bytes_logical()
+        chunk = _roofline("prefill", pre_flops, dom["prefill"], name)
+        e["roofline_chunk"] = chunk
+        # lower bounds of the step at the peaks: decode and chunk overlapped, or serialised
+        t_dec = dec_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_chk = pre_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+        e["step_bound_us"] = {"overlapped": max(t_dec, t_chk), "serialised": t_dec + t_chk}
+    if name == "long_decode_70b":
+        e["config"]["pool_holds_tokens"] = wl.num_blocks * 16
+    e["kernels_us"] = res["kernels_us"]
+    if with_cpu:
+        log(f"[bench] {name}: CPU oracle")
+        if name == "prefill_8b":
+            seg = int(np.argsort(wl.new_tokens)[wl.num_seqs // 2])   # a median-length prompt
+            e["cpu_baseline"] = cpu_baseline_prefill(wl, seg)
+        elif name == "tiny_mixed":
+            e["cpu_baseline"] = cpu_baseline_step(wl, 200)
+        else:
+            e["cpu_baseline"] = cpu_baseline_decode(wl, cpu_sample or 4)
+            if name == "cb_step_8b":
+                e["cpu_baseline_chunk"] = cpu_baseline_prefill(wl, int(pre[0]), rows=256)
+    return e
+
+
+CPU_SAMPLE = {"long_decode_70b": 3, "decode_8b": 64, "cb_step_8b": 16, "spec_verify_8b": 8,
+              "spec_verify_70b": 8}
 
 
 def main():
@@ -433,18 +711,24 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode_8b", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-batch line item")
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(DESCRIPTIONS),
+                    help="all (default): the long-context decode batch as the headline and the "
+                         "other four workloads as line items; or one workload alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=160, help="decode requests the oracle runs")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--group-members", type=int, default=0,
                     help="most members of a shared-prefix group (0: automatic, 1: no groups)")
     ap.add_argument("--pmc-summary", action="store_true",
                     help="summarise four rocprofv3 counter runs (see --fetch .. --calib-write)")
     ap.add_argument("--trace-summary", action="store_true",
-                    help="summarise a rocprofv3 kernel-trace CSV of the default bench (--trace DIR)")
+                    help="summarise a rocprofv3 kernel-trace CSV of a bench run (--trace DIR)")
     ap.add_argument("--trace")
+    ap.add_argument("--mfma-summary", action="store_true",
+                    help="summarise a rocprofv3 run with MFMA counters and a kernel trace "
+                         "(--counters DIR --trace DIR)")
+    ap.add_argument("--counters")
+    ap.add_argument("--cus", type=int, default=256)
+    ap.add_argument("--xcds", type=int, default=8)
     ap.add_argument("--kernel", default="decode_kernel")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
@@ -459,6 +743,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args)
+        return
+    if args.mfma_summary:
+        mfma_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -483,82 +770,26 @@ def main():
     log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs")
 
-    main_res = measure(args.workload, args.steps, args.warmup)
-    wl = main_res["wl"]
-    ms = main_res["ms"]
-    us = main_res["us"]
-    dom_us = main_res["dom_us"]
-    kv_bytes = wl.kv_bytes_unique()
-    flops = wl.attention_flops()
-    # segments on the split-context decode path: n * G <= 32 and n <= 8
-    max_dec = min(8, 32 // (wl.num_q_heads // wl.num_kv_heads))
-    decode_segs = np.nonzero((wl.new_tokens >= 1) & (wl.new_tokens <= max_dec))[0]
-    prefill_segs = np.nonzero(wl.new_tokens > max_dec)[0]
-    dec_bytes = int(wl.seq_lens[decode_segs].astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
-    if wl.shared_prefix:
-        dec_bytes = kv_bytes - int(wl.seq_lens[prefill_segs].astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
-    pre_flops = wl.attention_flops(segments=prefill_segs) if prefill_segs.size else 0
-
-    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+    plan = run_plan(args.workload, args.steps, args.warmup)
+    entries = {}
+    for name, steps, warmup, _ in plan:
+        entries[name] = bench_workload(name, steps, warmup, not args.no_cpu_baseline,
+                                       CPU_SAMPLE.get(name))
+    head_name = plan[0][0]
+    head = entries[head_name]
+    out = {"metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+           "higher_is_better": head["unit"] != "us/step", "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic"}
-    cfg = {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
-           "num_seqs": wl.num_seqs, "num_tokens": wl.num_tokens,
-           "heads": [wl.num_q_heads, wl.num_kv_heads], "head_dim": wl.head_dim,
-           "block_size": 16, "pool_blocks": wl.num_blocks,
-           "kv_bytes": kv_bytes, "attention_flops": flops}
-    if args.workload == "prefill_8b":
-        out.update(value=flops / (ms * 1e-3) / 1e12, unit="TFLOP/s")
-        ach = pre_flops / (dom_us * 1e-6) / 1e12
-        out["roofline"] = {"kernel": "prefill_kernel<128>", "bound": "mfma", "achieved": ach,
-                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / MFMA_BF16_PEAK_TFLOPS, "kernel_us": dom_us,
-                           "traffic": stored_traffic("prefill_kernel", args.workload)}
-    elif args.workload == "tiny_mixed":
-        out.update(value=kv_bytes / (ms * 1e-3) / 1e9, unit="GB/s")
-        out["roofline"] = None
-    else:
-        out.update(value=kv_bytes / (ms * 1e-3) / 1e9, unit="GB/s")
-        ach = dec_bytes / (dom_us * 1e-6) / 1e9
-        out["roofline"] = {"kernel": "decode_kernel<128>", "bound": "hbm", "achieved": ach,
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                           "kernel_us": dom_us,
-                           "traffic": stored_traffic("decode_kernel", args.workload),
-                           "algorithmic_bytes": dec_bytes}
+    cfg = dict(head["config"])
+    cfg = {"workload": head["workload"], **cfg}
     out["config"] = cfg
-    out["kernels_us"] = us
-    if args.workload == "long_decode_70b":
-        cfg["pool_holds_tokens"] = main_res["pool_tokens"]
-    if args.workload == "cb_step_8b":
-        cfg["kv_bytes_logical"] = wl.kv_bytes_logical()
-        out["chunk_prefill_tflops"] = pre_flops / (us["prefill"] * 1e-6) / 1e12
-
-    if args.workload == "decode_8b" and not args.no_prefill:
-        pr = measure("prefill_8b", max(5, args.steps // 2), args.warmup)
-        pwl = pr["wl"]
-        pflops = pwl.attention_flops()
-        ach = pflops / (pr["dom_us"] * 1e-6) / 1e12
-        out["prefill"] = {"workload": f"prefill_8b: {DESCRIPTIONS['prefill_8b']}",
-                          "ms_per_step": pr["ms"], "attention_flops": pflops,
-                          "tflops_step": pflops / (pr["ms"] * 1e-3) / 1e12,
-                          "roofline": {"kernel": "prefill_kernel<128>", "bound": "mfma",
-                                       "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS,
-                                       "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                                       "kernel_us": pr["dom_us"],
-                                       "traffic": stored_traffic("prefill_kernel", "prefill_8b")},
-                          "kernels_us": pr["us"]}
-
-    if not args.no_cpu_baseline:
-        if args.workload in ("decode_8b", "long_decode_70b", "cb_step_8b", "spec_verify_8b",
-                             "spec_verify_70b"):
-            import workloads
-            base_wl = workloads.make("decode_8b") if args.workload == "decode_8b" else wl
-            if args.workload == "decode_8b":
-                out["cpu_baseline"] = cpu_baseline_decode(base_wl, args.cpu_sample)
-            else:
-                out["cpu_baseline"] = cpu_baseline_decode(base_wl, 4)
-        elif args.workload == "prefill_8b":
-            out["cpu_baseline"] = prefill_cpu_baseline(wl)
+    for k in ("roofline", "roofline_chunk", "roofline_note", "step_bound_us", "cpu_baseline",
+              "cpu_baseline_chunk", "step_us_median", "step_us_min", "kernels_us"):
+        if k in head:
+            out[k] = head[k]
+    if len(plan) > 1:
+        out["items"] = {n: entries[n] for n, _, _, _ in plan[1:]}
     print(json.dumps(out), flush=True)
 
 
