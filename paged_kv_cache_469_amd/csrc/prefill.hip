@@ -44,6 +44,13 @@ namespace {
 constexpr int kKeys = 64;           // keys per tile
 constexpr int kWaves = 8;
 constexpr float kLazyMax = 8.f;     // how far (log2 units) m may trail the true maximum
+// MFMAs by which the LDS operand reads of the matrix phase run ahead
+#ifndef PKV_QK_LEAD
+#define PKV_QK_LEAD 3
+#endif
+#ifndef PKV_PV_LEAD
+#define PKV_PV_LEAD 3
+#endif
 
 template <int D>
 struct Geo {
@@ -242,7 +249,7 @@ __device__ __forceinline__ void qk(f32x16 (&s)[2], const u32x4 (&q)[Geo<D>::NSL]
       s[kt] = mfma32(k, q[sl], sl == 0 ? f32x16{} : s[kt]);
     }
   }
-  pipe_order<2 * G::NSL, 1, 3, VALU>();
+  pipe_order<2 * G::NSL, 1, PKV_QK_LEAD, VALU>();
 }
 
 // Scale O by alpha in the lanes whose maximum moved (a divergent branch:
@@ -276,7 +283,7 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2
       }
     }
   }
-  pipe_order<4 * G::NDT, 2, 3, VALU>();
+  pipe_order<4 * G::NDT, 2, PKV_PV_LEAD, VALU>();
 }
 
 // Online softmax of one tile, in two parts so the matrix phase can take
@@ -303,9 +310,19 @@ __device__ __forceinline__ float tile_max(f32x16 (&s)[2], int k0, int lim, int l
         s[kt][r] = fmaf(fminf(t, 0.f), 1e38f, s[kt][r]);
       }
   }
-  float mx = fmaxf(s[0][0], s[1][0]);
+  // a tree of three-input maxima (v_max3_f32): 16 instructions for 32 values
+  float a[11];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  for (int i = 0; i < 10; ++i) {
+    const int j = 3 * i;
+    a[i] = fmaxf(fmaxf(s[j / 16][j % 16], s[(j + 1) / 16][(j + 1) % 16]), s[(j + 2) / 16][(j + 2) % 16]);
+  }
+  a[10] = fmaxf(s[1][14], s[1][15]);
+  const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]);
+  const float b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+  const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]);
+  const float b3 = fmaxf(a[9], a[10]);
+  const float mx = fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
   return halves_max(mx);
 }
 
@@ -329,8 +346,9 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], float mx, u32x4 (
         const float e0 = fast_exp2(fmaf(s[kt][r], c, -mc));
         const float e1 = fast_exp2(fmaf(s[kt][r + 1], c, -mc));
         w[i] = pack_bf16(e0, e1);
-        sa += e0;
-        sb += e1;
+        const bool first = kt == 0 && u == 0 && i == 0;   // no add to a zero start
+        sa = first ? e0 : sa + e0;
+        sb = first ? e1 : sb + e1;
       }
       pr[kt][u] = u32x4{w[0], w[1], w[2], w[3]};
     }
@@ -385,7 +403,8 @@ struct Slots {
   PKV_LDS char* v[2];
 };
 
-// One tile step t (R = t % 3) of one wave: QK(t) and PV(t-1) on the
+// One tile step t (S = t % 6: the K slots cycle over three, the V slots over
+// two, so every slot address is a compile-time constant) of one wave: QK(t) and PV(t-1) on the
 // matrix cores, a barrier, the softmax of tile t, a barrier.  Group B runs
 // the same sequence one phase later (it passes one extra barrier first), so
 // each SIMD pairs one wave's matrix phase with the other's softmax.  With
@@ -404,7 +423,7 @@ struct Slots {
 // both.  The first readers of the new tiles (group A's QK(t+2) and
 // PV(t+1)) start after barrier 2t+4.  The products of both groups between
 // those barriers read the other slots.
-template <int D, int R>
+template <int D, int S>
 __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>& it, const Slots<D>& sl,
                                           int t, bool group_b, int wave, int lane,
                                           const u32x4 (&q)[Geo<D>::NSL], f32x16 (&o)[Geo<D>::NDT],
@@ -414,17 +433,22 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
                                           const CopyOff<D>& cv, int32_t (*bt)[kWindow],
                                           int& bt_next, uint32_t& bad, int& nxt, int& nxt_word,
                                           int n_items, int per_entry) {
-  constexpr int RK = R;             // K slot of tile t
-  constexpr int RP = (R + 2) % 3;   // K slot of tiles t - 1 and t + 2
+  constexpr int RK = S % 3;              // K slot of tile t
+  constexpr int RP = (RK + 2) % 3;       // K slot of tiles t - 1 and t + 2
+  constexpr int RV = (S % 2) ^ 1;        // V slot of tiles t - 1 and t + 1
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
   const int wq = wave & 3;
   // Matrix phase: QK(t) and PV(t-1), except that the first step has no P
   // yet and the last one no tile to score (wave-uniform branches).  A tile
   // the wave's queries do not see (past every key they see) has P = 0, and
   // every slot read holds finite values, so its products change nothing.
-  PKV_LDS char* const v_prev = (t & 1) ? sl.v[0] : sl.v[1];   // V slot of tiles t - 1 and t + 1
+  PKV_LDS char* const v_prev = sl.v[RV];
+  // The partner wave of this SIMD runs its softmax meanwhile: this wave's
+  // products go first when both have an instruction ready.
+  __builtin_amdgcn_s_setprio(1);
   if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
   if (t > 0) pv<D>(o, pr, av, v_prev);
+  __builtin_amdgcn_s_setprio(0);
   if (!group_b) {
     // after the products are issued, while the last of them run
     const int bk = 4 * (t + 2) + wq;   // block of K(t+2)
@@ -578,11 +602,16 @@ template <int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
   using G = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) char k0_lds[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k1_lds[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k2_lds[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v0_lds[G::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v1_lds[G::TILEB];
+  // The slots are aligned to their size, above the 1024 of the queries'
+  // area, so they are laid out first, at the bottom of the LDS: the matrix
+  // phase addresses them with a lane's offset in a register and the slot's
+  // base in the instruction's 16-bit offset field, with no address
+  // arithmetic between the operand reads.
+  __shared__ __attribute__((aligned(G::TILEB))) char k0_lds[G::TILEB];
+  __shared__ __attribute__((aligned(G::TILEB))) char k1_lds[G::TILEB];
+  __shared__ __attribute__((aligned(G::TILEB))) char k2_lds[G::TILEB];
+  __shared__ __attribute__((aligned(G::TILEB))) char v0_lds[G::TILEB];
+  __shared__ __attribute__((aligned(G::TILEB))) char v1_lds[G::TILEB];
   // per wave: its queries on their way in, its output on its way out
   __shared__ __attribute__((aligned(1024))) char io_lds[kWaves][32 * G::ROWB];
   __shared__ PrefillItem s_desc[2];   // the current and the next item
@@ -595,6 +624,9 @@ prefill_kernel(PrefillParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool group_b = wave >= kWaves / 2;
+#ifdef PKV_AGPR_HINT
+  asm volatile("" ::: "a0");   // lets the register allocator place MFMA accumulators in AGPRs
+#endif
   const int per_entry = (p.hkv / p.num_queues) * p.head_chunks;
   const int queue = blockIdx.x % p.num_queues;
   const int n_items = p.hdr->n_prefill * per_entry;
@@ -681,13 +713,23 @@ prefill_kernel(PrefillParams p) {
     // asked for only now, so the wait for the copies above does not include it
     if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[queue], 1);
     if (group_b) wg_barrier();
-    for (int t = 0; t <= it.ntiles; t += 3) {
-      tile_step<D, 0>(p, it, sl, t, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
+#define PKV_STEP(S)                                                                          \
+  tile_step<D, S>(p, it, sl, t + S, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, \
+                  cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry)
+    for (int t = 0; t <= it.ntiles; t += 6) {
+      PKV_STEP(0);
       if (t + 1 > it.ntiles) break;
-      tile_step<D, 1>(p, it, sl, t + 1, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
+      PKV_STEP(1);
       if (t + 2 > it.ntiles) break;
-      tile_step<D, 2>(p, it, sl, t + 2, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry);
+      PKV_STEP(2);
+      if (t + 3 > it.ntiles) break;
+      PKV_STEP(3);
+      if (t + 4 > it.ntiles) break;
+      PKV_STEP(4);
+      if (t + 5 > it.ntiles) break;
+      PKV_STEP(5);
     }
+#undef PKV_STEP
     copies_landed<0>();     // nothing in flight into the slots past the item
     if (!group_b) wg_barrier();   // group B's last step ends here
     if (wave == kWaves / 2) {
