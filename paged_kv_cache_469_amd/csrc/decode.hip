@@ -423,11 +423,15 @@ decode_kernel(DecodeParams p) {
 // per (segment, query head), for each of the segment's new tokens; lanes
 // split d.  The weights exp2(m_p - max m) rescale each partition's sum and
 // output to the common maximum (a partition none of whose keys a token sees
-// has m_p = -inf and weight 0; partition 0 always holds key 0).
+// has m_p = -inf and weight 0; partition 0 always holds key 0).  Lane i
+// holds the weight of partitions i, i + 64, ...; the partials' rows are read
+// eight partitions at a time, so their loads overlap instead of paying one
+// memory round trip per partition.
 template <int D>
 __global__ void __launch_bounds__(256)
 decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
   constexpr int PER = D / 64;
+  constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63;
   const int hchunks = (p.hq + 3) / 4;
   const int s = blockIdx.x / hchunks;
@@ -457,13 +461,31 @@ decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int i = 0; i < nparts; ++i) {
-      const int64_t slot = base + (int64_t)i * p.hq;
-      const float mp = p.part_ml[slot].x;
-      const float w = mp == -INFINITY ? 0.f : exp2f(mp - mx);
-      const float* src = p.part_o + slot * D + lane * PER;
+    for (int i0 = 0; i0 < nparts; i0 += 64) {
+      // weight of partition i0 + lane
+      float wl = 0.f;
+      if (i0 + lane < nparts) {
+        const float mp = p.part_ml[base + (int64_t)(i0 + lane) * p.hq].x;
+        wl = mp == -INFINITY ? 0.f : exp2f(mp - mx);
+      }
+      const int cnt = min(64, nparts - i0);
+      for (int j0 = 0; j0 < cnt; j0 += kBatch) {
+        float v[kBatch][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * src[e];
+        for (int j = 0; j < kBatch; ++j) {
+          const int i = i0 + min(j0 + j, cnt - 1);   // past the end: a repeated row, weight 0 below
+          const float* src = p.part_o + (base + (int64_t)i * p.hq) * D + lane * PER;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) v[j][e] = src[e];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const float w = __shfl(wl, min(j0 + j, 63));
+          const float wj = j0 + j < cnt ? w : 0.f;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] += wj * v[j][e];
+        }
+      }
     }
     const float inv = 1.f / den;
     uint16_t* dst = p.out + ((int64_t)(c0 + ti) * p.hq + hq) * D + lane * PER;

@@ -677,10 +677,12 @@ prefill_kernel(PrefillParams p) {
   // window 0, written when the item runs.  (The first step runs no PV, so the
   // other V slot is not read before V(1) lands in it.)
   auto start_item = [&](const Item<D>& nx, const PrefillItem* d) {
-    copy_queries<D>(p, nx.tok0, nx.qw, nx.n, nx.head, lane, lds_addr(io));
+    // the descriptor's block ids are read before any copy is issued: the
+    // wait for an LDS read would otherwise also wait for the copies
     const int bid0 = __builtin_amdgcn_readfirstlane(d->bid[wq]);
     const int bid1 = __builtin_amdgcn_readfirstlane(d->bid[4 + wq]);   // block of tile 1
     if (group_b) bt_next = window_entry(nx.bt_row, 0, wave - kWaves / 2, lane, nx.nblk);
+    copy_queries<D>(p, nx.tok0, nx.qw, nx.n, nx.head, lane, lds_addr(io));
     if (!group_b) {
       copy_block<D>(p, bid0, kBlock * wq, nx.kmax, nx.g, false, ck,
                     lds_addr(sl.k[0]) + wq * kBlock * G::ROWB, bad);
