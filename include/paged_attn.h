@@ -193,7 +193,7 @@ int paged_attention_device_status(const void* workspace, uint32_t* status,
                                   hipStream_t stream);
 
 /* Tokens per decode partition: 0 = automatic (the default), otherwise a
- * multiple of 32 in [32, 1024].  A tuning knob for measurements; it changes
+ * multiple of 32 in [32, 2048].  A tuning knob for measurements; it changes
  * only the split of long decode contexts, not the result beyond rounding.
  * It applies to the later paged_attention and paged_attention_workspace_size
  * calls of the calling thread only (other threads keep their own setting; a

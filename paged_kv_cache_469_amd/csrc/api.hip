@@ -64,14 +64,20 @@ int32_t group_members(int32_t group) {
 // that still gives at least 8192 wave-sized items for the longest allowed
 // context (the items then outnumber the chip's resident waves several times,
 // so the dynamic queue balances the tail); long partitions keep the merge's
-// extra traffic, about G * (D + 2) * 8 bytes per partition, under 2 %.
+// extra traffic, about G * (D + 2) * 8 bytes per partition, under 2 %.  2048
+// when that still gives 16384 items (long contexts): an item's start (its
+// queries, block ids and first K/V latency) and the partials are then paid
+// half as often, and twice the items keep the tail of the longer ones short.
 int32_t partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks) {
   const int32_t forced = g_part_tokens;
   if (forced > 0) return forced;
   const int64_t max_len = (int64_t)max_blocks * kBlock;
+  const auto items = [&](int32_t p) {
+    return (int64_t)num_seqs * num_kv_heads * ((max_len + p - 1) / p);
+  };
+  if (items(2048) >= 16384) return 2048;
   for (int32_t p : {1024, 512, 256, 128}) {
-    const int64_t items = (int64_t)num_seqs * num_kv_heads * ((max_len + p - 1) / p);
-    if (items >= 8192) return p;
+    if (items(p) >= 8192) return p;
   }
   return 64;
 }
@@ -501,8 +507,8 @@ int paged_attention_device_status(const void* workspace, uint32_t* status, hipSt
 }
 
 int paged_attention_set_partition_tokens(int32_t tokens) {
-  if (tokens != 0 && (tokens < 32 || tokens > 1024 || tokens % 32))
-    return fail(PAGED_EINVAL, "partition tokens must be 0 or a multiple of 32 in [32, 1024]");
+  if (tokens != 0 && (tokens < 32 || tokens > 2048 || tokens % 32))
+    return fail(PAGED_EINVAL, "partition tokens must be 0 or a multiple of 32 in [32, 2048]");
   g_part_tokens = tokens;
   return PAGED_OK;
 }

@@ -200,11 +200,14 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
       qf[c][sl] = rm.live[c] ? *reinterpret_cast<const u32x4*>(qrow + 32 * sl) : z;
     }
   }
-  // the partition's block ids, one per lane (P <= 1024 keys = 64 blocks)
+  // the partition's block ids, lane i holding entries i and 64 + i
+  // (P <= 2048 keys = 128 blocks)
   const int nblk = (key1 - key0 + kBlock - 1) / kBlock;
-  int my_bid = -1;
+  int my_bid = -1, my_bid2 = -1;
   if (lane < nblk) my_bid = bt_row[key0 / kBlock + lane];
-  const bool bad_bid = lane < nblk && (my_bid < 0 || (int64_t)my_bid >= p.num_blocks);
+  if (64 + lane < nblk) my_bid2 = bt_row[key0 / kBlock + 64 + lane];
+  const bool bad_bid = (lane < nblk && (my_bid < 0 || (int64_t)my_bid >= p.num_blocks)) ||
+                       (64 + lane < nblk && (my_bid2 < 0 || (int64_t)my_bid2 >= p.num_blocks));
   if (__any(bad_bid)) {
     if (lane == 0) atomicOr(&p.hdr->status, 2u);
   }
@@ -224,7 +227,10 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
   auto block_at = [&](int kb, int b, bool& ok) -> BlockRs {
     const int first = kb + kBlock * b;
     const int nvalid = min(max(key1 - first, 0), kBlock);
-    const int bid = nvalid > 0 ? __builtin_amdgcn_readlane(my_bid, (first - key0) / kBlock) : -1;
+    const int e = (first - key0) / kBlock;   // wave-uniform
+    const int bid = nvalid <= 0 ? -1
+                    : e < 64   ? __builtin_amdgcn_readlane(my_bid, e)
+                               : __builtin_amdgcn_readlane(my_bid2, e - 64);
     ok = nvalid > 0 && bid >= 0 && (int64_t)bid < p.num_blocks;
     return block_rs(p.cache, bid, ok, nvalid, block_bytes, row_bytes, g, D * 2);
   };
@@ -328,17 +334,18 @@ __device__ __forceinline__ void group_item(const DecodeParams& p, const GroupIte
   const int nmem = gi.nmem;
   const int key0 = part * p.part_tokens;
   const int key1 = key0 + p.part_tokens;
-  const int npb = p.part_tokens / kBlock;   // <= 64: one id per lane
-  int ids[8];
+  const int npb = p.part_tokens / kBlock;   // <= 128: two ids per lane
+  int ids[8], ids2[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int32_t* row = p.bt + (int64_t)gi.seg[i] * p.width + key0 / kBlock;
     ids[i] = (i < nmem && lane < npb) ? row[lane] : 0;
+    ids2[i] = (i < nmem && 64 + lane < npb) ? row[64 + lane] : 0;
   }
   uint32_t differ = 0;
 #pragma unroll
   for (int i = 1; i < 8; ++i)
-    if (i < nmem && __any(ids[i] != ids[0])) differ |= 1u << i;
+    if (i < nmem && __any(ids[i] != ids[0] || ids2[i] != ids2[0])) differ |= 1u << i;
   RowMap<CT> rm;
 #pragma unroll
   for (int c = 0; c < CT; ++c) {

@@ -69,7 +69,7 @@ struct DecodeParams {
   int64_t num_blocks;
   int32_t width;           // block table row length
   int32_t hq, hkv, group;
-  int32_t part_tokens;     // P, a multiple of 32, <= 1024
+  int32_t part_tokens;     // P, a multiple of 32, <= 2048
   int32_t pmax;
   float scale_log2;        // scale * log2(e)
 };

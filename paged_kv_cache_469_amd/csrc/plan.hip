@@ -193,7 +193,7 @@ __device__ __forceinline__ int cost_key(int n, int L, int qt, int qtile) {
 __device__ __forceinline__ int decode_bucket(int keys, int part_tokens) {
   return 1 + (part_tokens - keys) / 32;
 }
-constexpr int kDecodeBuckets = 1024 / 32 + 2;
+constexpr int kDecodeBuckets = 2048 / 32 + 2;   // partitions of up to 2048 keys
 
 __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   __shared__ int scratch[17];

@@ -143,6 +143,15 @@ CASES = {
     # first entry (the plan's links stop there) and inside it (the decode
     # kernel finds it and computes that member's partition on its own)
     "mixed_runs": (_mixed_runs, 256, [(11, 2 * 16), (7, 2 * 16 + 3)]),
+    # partitions of 2048 keys (128 blocks, two ids per lane): two shared
+    # partitions; in the second case one member's entry 69 (upper half of the
+    # first partition) points at a copy, which only the second id of a lane
+    # reveals
+    "p2048": (lambda: build("p2048", 2, 32, 8, 128, [(1, 4200 + 97 * i) for i in range(9)],
+                            shared_prefix=4096, shared_requests=tuple(range(9))), 2048, None),
+    "p2048_copy": (lambda: build("p2048_copy", 2, 32, 8, 128, [(1, 4200 + 97 * i) for i in range(9)],
+                                 shared_prefix=4096, shared_requests=tuple(range(9)), num_blocks=2400),
+                   2048, [(3, 69)]),
 }
 
 

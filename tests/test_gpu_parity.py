@@ -92,7 +92,7 @@ def test_edge_shapes(name, kw):
     check_close(out, ref, name)
 
 
-@pytest.mark.parametrize("tokens", [32, 64, 256, 1024])
+@pytest.mark.parametrize("tokens", [32, 64, 256, 1024, 2048])
 def test_partition_sizes(tokens):
     wl = workloads.make("long_decode_70b", num_requests=3, ctx=(3000, 9000))
     log(f"case partition {tokens}")
@@ -128,7 +128,7 @@ MULTI = [
 ]
 
 
-@pytest.mark.parametrize("tokens", [32, 256, 0])
+@pytest.mark.parametrize("tokens", [32, 256, 2048, 0])
 @pytest.mark.parametrize("name,kw", MULTI, ids=[m[0] for m in MULTI])
 def test_multi_token_decode(name, kw, tokens):
     wl = _custom(kw["hq"], kw["hkv"], kw["d"], kw["segs"], cfg=51, num_blocks=None)
