@@ -278,6 +278,9 @@ int attention_impl(const char* who, const void* q, const void* kv_cache,
   pp.width = max_blocks_per_seq;
   pp.max_len = max_blocks_per_seq * kBlock;
   pp.part_tokens = l.part_tokens;
+  // automatic choice of 1024 keys: the plan doubles it when no shared-prefix
+  // group can form (the workspace for 1024 holds the partials of 2048)
+  pp.part_double = (g_part_tokens == 0 && l.part_tokens == 1024) ? 1 : 0;
   pp.query_tile = query_tile;
   pp.decode_cap = (int32_t)l.decode_cap;
   pp.prefill_cap = (int32_t)l.prefill_cap;

@@ -32,7 +32,8 @@ struct WsHeader {
   int32_t decode_next;              // dynamic scheduling counter of the decode kernel
   int32_t prefill_next[kMaxQueues]; // dynamic scheduling counters of the prefill kernel
   int32_t n_group;                  // shared-prefix group items (first segment, partition, members)
-  int32_t pad0[3];
+  int32_t part_tokens;              // decode partition size the plan chose for this call
+  int32_t pad0[2];
   uint32_t zeros[16];               // 64 zero bytes: the source of K/V rows never loaded
   int32_t pad1[32];
 };

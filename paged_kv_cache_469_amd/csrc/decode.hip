@@ -298,12 +298,12 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
 // new tokens: row 16c + m is (token ti, head hh) of the segment and sees the
 // partition's keys up to its own position (causal in the segment).
 template <int D, int CT>
-__device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int part, int g, int lane,
-                                            int L, int tok, int n, int row0, int64_t row_bytes,
-                                            int64_t block_bytes) {
-  const int key0 = part * p.part_tokens;
-  const int key1 = min(L, key0 + p.part_tokens);
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int P, int s, int part, int g,
+                                            int lane, int L, int tok, int n, int row0,
+                                            int64_t row_bytes, int64_t block_bytes) {
+  const int key0 = part * P;
+  const int key1 = min(L, key0 + P);
+  const int nparts = (L + P - 1) / P;
   RowMap<CT> rm;
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
@@ -328,13 +328,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int s, int pa
 // each member's own partial row.  A member whose ids differ is computed on
 // its own afterwards, from its own table.
 template <int D, int CT>
-__device__ __forceinline__ void group_item(const DecodeParams& p, const GroupItem& gi, int g,
+__device__ __forceinline__ void group_item(const DecodeParams& p, int P, const GroupItem& gi, int g,
                                            int lane, int64_t row_bytes, int64_t block_bytes) {
   const int part = gi.part;
   const int nmem = gi.nmem;
-  const int key0 = part * p.part_tokens;
-  const int key1 = key0 + p.part_tokens;
-  const int npb = p.part_tokens / kBlock;   // <= 128: two ids per lane
+  const int key0 = part * P;
+  const int key1 = key0 + P;
+  const int npb = P / kBlock;   // <= 128: two ids per lane
   int ids[8], ids2[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -393,6 +393,7 @@ decode_kernel(DecodeParams p) {
   if (n_items == 0) return;   // no decode segment in this step: no queue traffic
   const int64_t row_bytes = (int64_t)p.hkv * D * 2;
   const int64_t block_bytes = 2 * kBlock * row_bytes;
+  const int P = wave_uniform(p.hdr->part_tokens);   // the plan's partition size
 
   for (;;) {
     int it = 0;
@@ -403,9 +404,9 @@ decode_kernel(DecodeParams p) {
       const GroupItem gi = p.groups[it / p.hkv];
       const int g = it % p.hkv;
       if (gi.nmem * p.group <= 16)
-        group_item<D, 1>(p, gi, g, lane, row_bytes, block_bytes);
+        group_item<D, 1>(p, P, gi, g, lane, row_bytes, block_bytes);
       else
-        group_item<D, 2>(p, gi, g, lane, row_bytes, block_bytes);
+        group_item<D, 2>(p, P, gi, g, lane, row_bytes, block_bytes);
       continue;
     }
     it -= n_grp;
@@ -420,9 +421,9 @@ decode_kernel(DecodeParams p) {
     if (row0 < 0) continue;          // skipped by the plan (and flagged there)
     // 16 or 32 query rows (n * G of them live)
     if (n * p.group <= 16)
-      decode_item<D, 1>(p, s, part, g, lane, L, tok, n, row0, row_bytes, block_bytes);
+      decode_item<D, 1>(p, P, s, part, g, lane, L, tok, n, row0, row_bytes, block_bytes);
     else
-      decode_item<D, 2>(p, s, part, g, lane, L, tok, n, row0, row_bytes, block_bytes);
+      decode_item<D, 2>(p, P, s, part, g, lane, L, tok, n, row0, row_bytes, block_bytes);
   }
 }
 
@@ -450,7 +451,8 @@ decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
   const int c1 = p.cu[s + 1];
   const int L = p.lens[s];
   if (c0 < 0 || c1 > num_tokens || c1 <= c0 || L < c1 - c0 || L > p.width * kBlock) return;
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  const int P = p.hdr->part_tokens;   // the plan's partition size
+  const int nparts = (L + P - 1) / P;
   if (nparts <= 1) return;
   for (int ti = 0; ti < c1 - c0; ++ti) {
     const int64_t base = (int64_t)(row0 + ti) * p.pmax * p.hq + hq;   // slot of partition 0

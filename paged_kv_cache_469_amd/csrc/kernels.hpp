@@ -42,7 +42,8 @@ struct PlanParams {
   int32_t num_tokens;
   int32_t width;         // block-table row length
   int32_t max_len;       // max_blocks_per_seq * 16
-  int32_t part_tokens;   // P
+  int32_t part_tokens;   // P chosen by the host (the workspace is sized for it)
+  int32_t part_double;   // 1: use 2P when no two decode segments share a first block
   int32_t query_tile;    // QT
   int32_t decode_cap;    // capacity of decode_items
   int32_t prefill_cap;   // capacity of prefill_items
@@ -69,7 +70,7 @@ struct DecodeParams {
   int64_t num_blocks;
   int32_t width;           // block table row length
   int32_t hq, hkv, group;
-  int32_t part_tokens;     // P, a multiple of 32, <= 2048
+  int32_t part_tokens;     // P chosen by the host; the kernels use the plan's (header)
   int32_t pmax;
   float scale_log2;        // scale * log2(e)
 };

@@ -238,7 +238,14 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   // (the first 1024 segments of a larger batch are grouped among themselves)
   const bool grouping = p.group_max >= 2;
   si0 = seg_info(p, threadIdx.x);
-  if (grouping) {
+  // The partition size: the host's P, or 2P (when the host allows it) if no
+  // two single-token decode segments of more than one partition start with
+  // the same block, that is, when no shared-prefix group can form: longer
+  // partitions pay an item's start and its partials half as often.  The
+  // hash pass below finds whether two such first entries are equal; it runs
+  // whether or not grouping is on, so the choice does not depend on it.
+  int P = p.part_tokens;
+  if (grouping || p.part_double) {
     const int s = threadIdx.x;
     const bool elig0 = si0.ok && si0.n == 1 && si0.L > p.part_tokens;
     // a table entry is read only below ceil(L / 16)
@@ -266,7 +273,9 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     // each distinct first entry owns one slot, so equal slots mean equal
     // first entries; sorting by (slot, index) keeps the segments of one
     // first entry together, in index order
-    if (__syncthreads_or(dup)) {
+    const bool any_dup = __syncthreads_or(dup);
+    if (!any_dup && p.part_double) P = 2 * p.part_tokens;
+    if (grouping && any_dup) {
       // bitonic sort of (slot, index) over the first nsort positions (a
       // power of two >= the number of segments, at most 1024; ineligible
       // segments sort last).  Thread s holds position s; its partner s ^ j
@@ -306,11 +315,14 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       if (cand) g_cand[ci] = r;
       __syncthreads();
       // link of each candidate position: how many leading full partitions
-      // its segment has whose first block ids equal the previous position's.
-      // Only the first id of a partition is compared here (one pair of loads
-      // per partition, all in one trip to memory); the decode kernel compares
-      // a grouped partition's ids whole and computes a member that differs
-      // on its own.  Rounds of 8 partitions: a unit is (candidate,
+      // its segment has whose first and last block ids equal the previous
+      // position's.  Only those two ids of a partition are compared here (two
+      // pairs of loads per partition, all in one trip to memory): a prefix
+      // shared by block tables covers whole blocks from the first, so a
+      // partition that the prefix ends inside has a differing last id and is
+      // not linked (the members would then each be computed on their own
+      // inside the group item).  The decode kernel compares a grouped
+      // partition's ids whole and computes a member that differs on its own.  Rounds of 8 partitions: a unit is (candidate,
       // partition); g_size holds a candidate's first differing partition,
       // g_cnt marks finished candidates.
       constexpr int kRound = 8;
@@ -329,7 +341,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
           if (!differ) {
             const int32_t* a = p.bt + (int64_t)g_seg[rc] * p.width + c * npb;
             const int32_t* b = p.bt + (int64_t)g_seg[rc - 1] * p.width + c * npb;
-            differ = a[0] != b[0];
+            differ = a[0] != b[0] || a[npb - 1] != b[npb - 1];
           }
           if (differ) atomicMin(&g_size[k], c);
         }
@@ -404,12 +416,12 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     if (s < p.num_seqs && !si.ok) {
       status |= 1u;
     } else if (si.ok && si.n >= 1 && si.n <= p.max_decode_n) {
-      const int parts = (si.L + p.part_tokens - 1) / p.part_tokens;
+      const int parts = (si.L + P - 1) / P;
       nd = parts - cov_s;
-      nfull = si.L / p.part_tokens - cov_s;
+      nfull = si.L / P - cov_s;
       nr = si.n;
-      if (parts * p.part_tokens > si.L)
-        atomicAdd(&dhist[decode_bucket(si.L - (parts - 1) * p.part_tokens, p.part_tokens)], 1);
+      if (parts * P > si.L)
+        atomicAdd(&dhist[decode_bucket(si.L - (parts - 1) * P, P)], 1);
     } else if (si.ok && si.n > p.max_decode_n) {
       np = min((si.n + p.query_tile - 1) / p.query_tile, p.prefill_cap + 1);
     }
@@ -495,7 +507,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     const int s = base + (int)threadIdx.x;
     const SegInfo si = base == 0 ? first : seg_info(p, s);
     const bool dec = si.ok && si.n >= 1 && si.n <= p.max_decode_n;
-    const int full = dec ? si.L / p.part_tokens : 0;
+    const int full = dec ? si.L / P : 0;
     const int cov_s = base == 0 ? cov : 0;   // partitions 0 .. cov_s - 1 are in group items
     int at = first_ofull;
     if (base == 0) {
@@ -508,8 +520,8 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     if (dec) {
       for (int i = cov_s; i < full; ++i)
         if (at + i - cov_s < p.decode_cap) p.decode_items[at + i - cov_s] = make_int2(s, i);
-      if (si.L > full * p.part_tokens) {
-        const int at2 = atomicAdd(&dhist[decode_bucket(si.L - full * p.part_tokens, p.part_tokens)], 1);
+      if (si.L > full * P) {
+        const int at2 = atomicAdd(&dhist[decode_bucket(si.L - full * P, P)], 1);
         if (at2 < p.decode_cap) p.decode_items[at2] = make_int2(s, full);
       }
     }
@@ -568,6 +580,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     p.hdr->n_decode = min(dec_base, p.decode_cap);
     p.hdr->n_prefill = min(pre_total, p.prefill_cap);
     p.hdr->n_group = n_group;
+    p.hdr->part_tokens = P;
     p.hdr->decode_next = 0;
   }
   if (threadIdx.x < kMaxQueues) p.hdr->prefill_next[threadIdx.x] = 0;

@@ -32,7 +32,8 @@ def _expected(wl, part, members, limit=1024):
     """(group items, ordinary decode items) of the grouping rule: the
     segments with one new token, more than one partition and a valid first
     block id, sorted by (first block id, index); neighbours in that order
-    link while their leading full partitions start with the same block id;
+    link while their leading full partitions start and end with the same
+    block ids;
     runs of links are cut into groups of `members`, and a group of two or
     more covers the partitions every neighbouring pair in it links.  Only
     the first `limit` segments are grouped.  (The decode kernel then compares
@@ -50,7 +51,8 @@ def _expected(wl, part, members, limit=1024):
         if tables[a, 0] == tables[b, 0]:
             full = min(lens[a], lens[b]) // part
             c = 0
-            while c < full and tables[a, c * npb] == tables[b, c * npb]:
+            while (c < full and tables[a, c * npb] == tables[b, c * npb]
+                   and tables[a, c * npb + npb - 1] == tables[b, c * npb + npb - 1]):
                 c += 1
             link[r] = c
     cov = [0] * s_count
@@ -143,6 +145,11 @@ CASES = {
     # first entry (the plan's links stop there) and inside it (the decode
     # kernel finds it and computes that member's partition on its own)
     "mixed_runs": (_mixed_runs, 256, [(11, 2 * 16), (7, 2 * 16 + 3)]),
+    # a shared prefix that ends inside a partition (1024 tokens at P = 2048):
+    # no partition is shared whole, so no group forms and each segment reads
+    # its own (the plan compares a partition's last id too)
+    "prefix_inside": (lambda: build("prefix_inside", 2, 32, 8, 128, [(1, 4200 + 97 * i) for i in range(9)],
+                                    shared_prefix=1024, shared_requests=tuple(range(9))), 2048, None),
     # partitions of 2048 keys (128 blocks, two ids per lane): two shared
     # partitions; in the second case one member's entry 69 (upper half of the
     # first partition) points at a copy, which only the second id of a lane
@@ -181,7 +188,10 @@ def test_groups_bitwise_and_parity(name):
         log(f"  members {m}: {n_group} group items, {n_decode} decode items (expected {want})")
         assert (n_group, n_decode) == want, f"members {m}"
         assert np.array_equal(out, runs[1][0]), f"members {m}: output differs from the ungrouped run"
-    assert runs[0][1][0] > 0, "the case must form groups"
+    if name == "prefix_inside":
+        assert runs[0][1][0] == 0, "a prefix that ends inside a partition must not group it"
+    else:
+        assert runs[0][1][0] > 0, "the case must form groups"
     assert pkv.paged_attention_device_status(st.ws) == 0
     ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens, wl.scale)
     check_close(runs[0][0], ref, f"groups {name}")
