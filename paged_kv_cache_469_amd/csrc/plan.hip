@@ -200,6 +200,7 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   __shared__ int scan5[17][5];
   __shared__ int hist[kCostBuckets];
   __shared__ int dhist[kDecodeBuckets];
+  __shared__ int dscan_total;
   // prefill segments of a batch of at most 1024 segments, listed so that one
   // wave per segment spreads its query tiles over the lanes
   __shared__ int pl_seg[1024], pl_n[1024], pl_len[1024], pl_c0[1024];
@@ -486,17 +487,27 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     __syncthreads();
   }
 
-  // pass 2: bucket offsets (exclusive scans of the histograms)
-  int unused;
-  hist[threadIdx.x] = block_exclusive_scan(hist[threadIdx.x], scratch, &unused);
-  if (threadIdx.x == 0) {
-    dhist[0] = full_base;
-    int run = 0;
-    for (int b = 0; b < kDecodeBuckets; ++b) {
-      const int c = dhist[b];
-      dhist[b] = run;
-      run += c;
+  // pass 2: bucket offsets (exclusive scans of the histograms): the decode
+  // buckets by the first two waves (one bucket per thread; bucket 0 holds
+  // the full partitions), the prefill cost buckets by the whole block, only
+  // when the step has prefill items (pre_total is the same in every thread)
+  int dc = 0, dx = 0;
+  if (threadIdx.x < 128) {   // whole waves 0 and 1
+    const int b = threadIdx.x;
+    dc = b == 0 ? full_base : (b < kDecodeBuckets ? dhist[b] : 0);
+    dx = dc;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(dx, off);
+      if (lane >= off) dx += y;
     }
+    if (threadIdx.x == 63) dscan_total = dx;   // buckets 0 .. 63
+  }
+  __syncthreads();
+  if (threadIdx.x < kDecodeBuckets) dhist[threadIdx.x] = (threadIdx.x >= 64 ? dscan_total : 0) + dx - dc;
+  if (pre_total > 0) {
+    int unused;
+    hist[threadIdx.x] = block_exclusive_scan(hist[threadIdx.x], scratch, &unused);
   }
   __syncthreads();
 
