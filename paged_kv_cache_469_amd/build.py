@@ -2,8 +2,9 @@
 
 Every ``csrc/*.hip`` file is compiled with hipcc and every ``csrc/*.cpp``
 file (host-only C++: the block manager) with g++, in parallel, and all are
-linked into one shared library next to this file.  Packed-FP32 instructions
-are switched off for all device code.
+linked into one shared library next to this file.  Each ``probes/*.hip``
+(a standalone measurement program) becomes an executable beside its source.
+Packed-FP32 instructions are switched off for all device code.
 """
 
 import concurrent.futures
@@ -58,11 +59,30 @@ def _compile(src):
     return obj
 
 
+PROBES = os.path.join(HERE, "probes")
+
+
+def _probe(src):
+    """A measurement probe: one standalone executable per probes/*.hip."""
+    exe = src[:-len(".hip")]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", src, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    return exe
+
+
 def build(verbose=False):
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    probes = sorted(os.path.join(PROBES, f) for f in os.listdir(PROBES) if f.endswith(".hip")) \
+        if os.path.isdir(PROBES) else []
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        probe_jobs = [ex.submit(_probe, p) for p in probes]
         objs = list(ex.map(_compile, srcs))
+        for j in probe_jobs:
+            j.result()
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
