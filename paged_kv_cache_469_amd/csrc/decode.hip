@@ -100,14 +100,22 @@ __device__ __forceinline__ void load_kv(KvRegs<D>& r, const BlockRs& b0, const B
   }
 }
 
+// How far (log2 units) the running maximum may trail a row's true maximum:
+// m moves only when a step's maximum exceeds it by more than this, so P stays
+// below 2^8 and O is rescaled only in the rare steps where some row's m moved.
+constexpr float kLazyMax = 8.f;
+
 // One step of 32 keys for CT column tiles of 16 query rows: the K fragments
 // are multiplied against every tile's queries and each V operand against
-// every tile's P, so the tiles share one read of K and V.
+// every tile's P, so the tiles share one read of K and V.  `edge` (wave-
+// uniform) is set for a step some row does not see whole (a partition's
+// last keys, a row's causal limit, a block outside the pool); the other
+// steps skip the per-key checks.
 template <int D, int CT>
 __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf)[CT][D / 32],
                                             f32x4 (&o)[CT][D / 16], float (&m_run)[CT],
                                             float (&l_run)[CT], int kb, const int (&kend)[CT],
-                                            bool ok0, bool ok1, int j, float scale_log2) {
+                                            bool edge, bool ok0, bool ok1, int j, float scale_log2) {
   constexpr int NS = D / 32;
   constexpr int NT = D / 16;
   f32x4 sc[CT][2];
@@ -121,37 +129,51 @@ __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf
       for (int c = 0; c < CT; ++c) sc[c][b] = mfma16(r.k[b][sl], qf[c][sl], sc[c][b]);
   }
   float alpha[CT];
+  bool moved = false;
   u32x4 pb[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     float x[8];
-    float cmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int b = i >> 2;
-      const bool okb = b ? ok1 : ok0;
-      const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < kend[c]);
-      x[i] = live ? sc[c][b][i & 3] * scale_log2 : -INFINITY;
-      cmax = fmaxf(cmax, x[i]);
+    for (int i = 0; i < 8; ++i) x[i] = sc[c][i >> 2][i & 3] * scale_log2;
+    if (edge) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int b = i >> 2;
+        const bool okb = b ? ok1 : ok0;
+        const bool live = okb && (kb + 16 * b + 4 * j + (i & 3) < kend[c]);
+        x[i] = live ? x[i] : -INFINITY;
+      }
     }
+    float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     cmax = wave_max_xor(cmax, 16);
     cmax = wave_max_xor(cmax, 32);
-    const float m_new = fmaxf(m_run[c], cmax);
-    // all keys so far left out (blocks skipped as invalid, or keys this row
-    // does not see yet): keep the state
-    const bool none = m_new == -INFINITY;
-    alpha[c] = none ? 1.f : exp2f(m_run[c] - m_new);
+    // m_run = -inf: no key seen yet (then O and l are zero, nothing to rescale)
+    const bool first = m_run[c] == -INFINITY;
+    const bool upd = first ? cmax != -INFINITY : cmax - m_run[c] > kLazyMax;
+    const float m_new = upd ? cmax : m_run[c];
+    alpha[c] = upd && !first ? __builtin_amdgcn_exp2f(m_run[c] - m_new) : 1.f;
+    moved = moved || (upd && !first);
+    // keys left out have x = -inf and P = 0; while no key was seen m stays
+    // -inf and every P is 0
+    const float mu = m_new == -INFINITY ? 0.f : m_new;
     float p[8];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = none ? 0.f : exp2f(x[i] - m_new);
+      p[i] = __builtin_amdgcn_exp2f(x[i] - mu);
       psum += p[i];
     }
     l_run[c] = l_run[c] * alpha[c] + psum;
     m_run[c] = m_new;
     pb[c] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                   pack_bf16(p[6], p[7])};
+  }
+  if (__any(moved)) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[c][t] *= alpha[c];
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -160,10 +182,7 @@ __device__ __forceinline__ void attend_step(const KvRegs<D>& r, const u32x4 (&qf
     u32x4 a = {pick_halves(r.v[0][w], r.v[1][w], hi), pick_halves(r.v[2][w], r.v[3][w], hi),
                pick_halves(r.v[4][w], r.v[5][w], hi), pick_halves(r.v[6][w], r.v[7][w], hi)};
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      o[c][t] *= alpha[c];
-      o[c][t] = mfma16(a, pb[c], o[c][t]);
-    }
+    for (int c = 0; c < CT; ++c) o[c][t] = mfma16(a, pb[c], o[c][t]);
   }
 }
 
@@ -178,11 +197,12 @@ struct RowMap {
 };
 
 // One work item: the keys key0 .. key1 - 1 of the block table row `bt_row`
-// for KV head g, attended by the query rows of `rm`.
+// for KV head g, attended by the query rows of `rm`; every row sees the keys
+// before kfull.
 template <int D, int CT>
 __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t* bt_row, int key0,
-                                            int key1, int part, bool direct, int g, int lane,
-                                            const RowMap<CT>& rm, int64_t row_bytes,
+                                            int key1, int kfull, int part, bool direct, int g,
+                                            int lane, const RowMap<CT>& rm, int64_t row_bytes,
                                             int64_t block_bytes) {
   constexpr int NS = D / 32;
   constexpr int NT = D / 16;
@@ -227,7 +247,7 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
   auto block_at = [&](int kb, int b, bool& ok) -> BlockRs {
     const int first = kb + kBlock * b;
     const int nvalid = min(max(key1 - first, 0), kBlock);
-    const int e = (first - key0) / kBlock;   // wave-uniform
+    const int e = min((first - key0) / kBlock, 127);   // wave-uniform
     const int bid = nvalid <= 0 ? -1
                     : e < 64   ? __builtin_amdgcn_readlane(my_bid, e)
                                : __builtin_amdgcn_readlane(my_bid2, e - 64);
@@ -241,20 +261,28 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
     const BlockRs x0 = block_at(key0, 0, ao0), x1 = block_at(key0, 1, ao1);
     load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
   }
-  for (int kb = key0; kb < key1; kb += 64) {
+  // Two register sets: the loads of the next 32 keys are issued before the
+  // current 32 are computed.  They are issued on every step, also past the
+  // partition's end (zero-range buffers: nothing is read), so the code has
+  // no branch around them and each step waits only for its own loads, not
+  // for the next step's as well.
+  for (int kb = key0;; kb += 64) {
     const int kn = kb + 32;
-    if (kn < key1) {
+    {
       const BlockRs x0 = block_at(kn, 0, bo0), x1 = block_at(kn, 1, bo1);
       load_kv<D>(rb, x0, x1, m, j, (uint32_t)row_bytes);
     }
-    attend_step<D, CT>(ra, qf, o, m_run, l_run, kb, kend, ao0, ao1, j, p.scale_log2);
+    attend_step<D, CT>(ra, qf, o, m_run, l_run, kb, kend, !(ao0 && ao1 && kb + 32 <= kfull), ao0, ao1, j,
+                       p.scale_log2);
     if (kn >= key1) break;
     const int kn2 = kb + 64;
-    if (kn2 < key1) {
+    {
       const BlockRs x0 = block_at(kn2, 0, ao0), x1 = block_at(kn2, 1, ao1);
       load_kv<D>(ra, x0, x1, m, j, (uint32_t)row_bytes);
     }
-    attend_step<D, CT>(rb, qf, o, m_run, l_run, kn, kend, bo0, bo1, j, p.scale_log2);
+    attend_step<D, CT>(rb, qf, o, m_run, l_run, kn, kend, !(bo0 && bo1 && kn + 32 <= kfull), bo0, bo1, j,
+                       p.scale_log2);
+    if (kn2 >= key1) break;
   }
 
 #pragma unroll
@@ -315,7 +343,9 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int P, int s,
     rm.hq[c] = g * p.group + (row - ti * p.group);
     rm.prow[c] = row0 + ti;
   }
-  decode_rows<D, CT>(p, p.bt + (int64_t)s * p.width, key0, key1, part, nparts == 1, g, lane, rm,
+  // every row sees the keys before L - n + 1 (the first new token's)
+  decode_rows<D, CT>(p, p.bt + (int64_t)s * p.width, key0, key1, min(key1, L - n + 1), part, nparts == 1,
+                     g, lane, rm,
                      row_bytes, block_bytes);
 }
 
@@ -362,7 +392,7 @@ __device__ __forceinline__ void group_item(const DecodeParams& p, int P, const G
     rm.hq[c] = g * p.group + (row - mi * p.group);
     rm.prow[c] = r0;
   }
-  decode_rows<D, CT>(p, p.bt + (int64_t)gi.seg[0] * p.width, key0, key1, part, false, g, lane, rm,
+  decode_rows<D, CT>(p, p.bt + (int64_t)gi.seg[0] * p.width, key0, key1, key1, part, false, g, lane, rm,
                      row_bytes, block_bytes);
   while (differ) {
     const int mi = __builtin_ctz(differ);
@@ -378,7 +408,7 @@ __device__ __forceinline__ void group_item(const DecodeParams& p, int P, const G
     one.qtok[0] = p.cu[sm];
     one.hq[0] = g * p.group + min(hh, p.group - 1);
     one.prow[0] = p.seg_row[sm];
-    decode_rows<D, 1>(p, p.bt + (int64_t)sm * p.width, key0, key1, part, false, g, lane, one,
+    decode_rows<D, 1>(p, p.bt + (int64_t)sm * p.width, key0, key1, key1, part, false, g, lane, one,
                       row_bytes, block_bytes);
   }
 }
