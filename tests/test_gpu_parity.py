@@ -160,6 +160,39 @@ def test_multi_token_decode_sharpened():
     check_close(out, ref, "multi-token sharpened")
 
 
+def test_running_maximum_jumps():
+    # keys whose scores sit far above everything before them (by 17 and 58
+    # log2 units, a third and nine tenths of the way through each sequence):
+    # the lazy running maximum of both kernels has to move late in an item and
+    # rescale O and l there (decode, a speculative check and a prompt)
+    segs = [(1, 3000), (1, 5000), (4, 4100), (1, 700), (100, 400)]
+    wl = _custom(32, 8, 128, segs, cfg=52, num_blocks=None)
+    log("case running maximum jumps")
+    st = DeviceStep(wl, host_pool=True)
+    cu, lens, bt, g_ = wl.cu_seqlens_q, wl.seq_lens, wl.block_tables, wl.group
+    qf = bf16.to_f64(st.q_host)
+    pool16 = st.pool.view(torch.int16)
+    for s in range(wl.num_seqs):
+        length, tok = int(lens[s]), int(cu[s + 1]) - 1   # the segment's last query sees every key
+        for frac, target in ((0.3, 12.0), (0.9, 40.0)):
+            pos = int(frac * (length - 1))
+            blk, row = int(bt[s, pos // 16]), pos % 16
+            for g in range(wl.num_kv_heads):
+                qv = qf[tok, g * g_]
+                bits = bf16.from_f64(qv * (target / (wl.scale * float(qv @ qv))))   # logit = target
+                st.host[blk, 0, row, g] = bits
+                pool16[blk, 0, row, g] = torch.from_numpy(bits.view(np.int16)).cuda()
+    ref = paged.attend(st.q_host, st.host, bt, cu, lens, wl.scale)
+    for tokens in (0, 256):
+        pkv.paged_attention_set_partition_tokens(tokens)
+        try:
+            out = down_u16(st.attend())
+        finally:
+            pkv.paged_attention_set_partition_tokens(0)
+        check_close(out, ref, f"maximum jumps P={tokens}")
+    assert st.status() == 0
+
+
 def test_more_than_1024_segments():
     # the plan kernel walks segments in chunks of 1024 threads: decode items,
     # partial rows and prefill items of later chunks take its second path
