@@ -403,6 +403,31 @@ struct Slots {
   PKV_LDS char* v[2];
 };
 
+// The workgroup's queue has run dry: its next item comes from the queue with
+// the most items left (that item's K/V are then not in this XCD's L2 but come
+// from HBM or the last-level cache), at the cost of one read of the eight
+// counters and one atomic.  A race that empties that queue too ends the
+// workgroup.
+__device__ __forceinline__ int steal_item(const PrefillParams& p, int n_items, int& nq, int lane) {
+  int left = -1;
+  if (lane < p.num_queues)
+    left = n_items - __hip_atomic_load(&p.hdr->prefill_next[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int best = 0, bq = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxQueues; ++k) {
+    const int lk = __builtin_amdgcn_readlane(left, k);
+    if (lk > best) {
+      best = lk;
+      bq = k;
+    }
+  }
+  if (best <= 0) return n_items;
+  int v = 0;
+  if (lane == 0) v = atomicAdd(&p.hdr->prefill_next[bq], 1);
+  nq = bq;
+  return __builtin_amdgcn_readfirstlane(__shfl(v, 0));
+}
+
 // One tile step t (S = t % 6: the K slots cycle over three, the V slots over
 // two, so every slot address is a compile-time constant) of one wave: QK(t) and PV(t-1) on the
 // matrix cores, a barrier, the softmax of tile t, a barrier.  Group B runs
@@ -431,7 +456,7 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
                                           float& l, const uint32_t (&ak)[Geo<D>::NSL],
                                           const uint32_t (&av)[Geo<D>::NDT], const CopyOff<D>& ck,
                                           const CopyOff<D>& cv, int32_t (*bt)[kWindow],
-                                          int& bt_next, uint32_t& bad, int& nxt, int& nxt_word,
+                                          int& bt_next, uint32_t& bad, int& nxt, int& nq, int& nxt_word,
                                           int n_items, int per_entry) {
   constexpr int RK = S % 3;              // K slot of tile t
   constexpr int RP = (RK + 2) % 3;       // K slot of tiles t - 1 and t + 2
@@ -469,6 +494,7 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
       // the next item: its index (asked for when this item started) and its
       // descriptor, one dword per lane, written to LDS when this item ends
       nxt = __builtin_amdgcn_readfirstlane(nxt);
+      if (nxt >= n_items && p.num_queues > 1) nxt = steal_item(p, n_items, nq, lane);
       const int32_t* src = reinterpret_cast<const int32_t*>(p.items + min(nxt, n_items - 1) / per_entry);
       nxt_word = src[lane & 15];
     }
@@ -616,6 +642,7 @@ prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char io_lds[kWaves][32 * G::ROWB];
   __shared__ PrefillItem s_desc[2];   // the current and the next item
   __shared__ int s_itx[2];
+  __shared__ int s_q[2];              // the queues they came from
   __shared__ int32_t s_bt[2][kWindow];   // block-table windows of the current item
   const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds, (PKV_LDS char*)k2_lds},
                        {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds}};
@@ -659,7 +686,10 @@ prefill_kernel(PrefillParams p) {
       const int32_t* src = reinterpret_cast<const int32_t*>(p.items + min(itx0, n_items - 1) / per_entry);
       reinterpret_cast<int32_t*>(&s_desc[0])[lane] = src[lane];
     }
-    if (lane == 0) s_itx[0] = itx0;
+    if (lane == 0) {
+      s_itx[0] = itx0;
+      s_q[0] = queue;
+    }
   }
   __syncthreads();
   int cur = 0;
@@ -697,6 +727,8 @@ prefill_kernel(PrefillParams p) {
 
   for (;;) {
     int nxt = 0, nxt_word = 0;   // wave 4: the next item's index and descriptor
+    const int cq = __builtin_amdgcn_readfirstlane(s_q[cur]);   // the queue of the current item
+    int nq = cq;                 // wave 4: the queue of the next item
     f32x16 o[G::NDT];
 #pragma unroll
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x16{};
@@ -713,11 +745,11 @@ prefill_kernel(PrefillParams p) {
     __syncthreads();   // K(0), K(1), V(0), window 0 in LDS
     read_queries<D>(q, io, lane, p.q_sign);
     // asked for only now, so the wait for the copies above does not include it
-    if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[queue], 1);
+    if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[cq], 1);
     if (group_b) wg_barrier();
 #define PKV_STEP(S)                                                                          \
   tile_step<D, S>(p, it, sl, t + S, group_b, wave, lane, q, o, sc, pr, alpha, m, l, ak, av, ck, \
-                  cv, s_bt, bt_next, bad, nxt, nxt_word, n_items, per_entry)
+                  cv, s_bt, bt_next, bad, nxt, nq, nxt_word, n_items, per_entry)
     for (int t = 0; t <= it.ntiles; t += 6) {
       PKV_STEP(0);
       if (t + 1 > it.ntiles) break;
@@ -736,13 +768,18 @@ prefill_kernel(PrefillParams p) {
     if (!group_b) wg_barrier();   // group B's last step ends here
     if (wave == kWaves / 2) {
       if (lane < 16) reinterpret_cast<int32_t*>(&s_desc[cur ^ 1])[lane] = nxt_word;
-      if (lane == 0) s_itx[cur ^ 1] = nxt;
+      if (lane == 0) {
+        s_itx[cur ^ 1] = nxt;
+        s_q[cur ^ 1] = nq;
+      }
     }
     __syncthreads();   // every slot read; the next item's descriptor in LDS
 
     const int itx_n = s_itx[cur ^ 1];
     const Item<D> prev = it;
-    if (itx_n < n_items) it = item_of<D>(p, &s_desc[cur ^ 1], itx_n, per_entry, queue, wave, lane);
+    if (itx_n < n_items)
+      it = item_of<D>(p, &s_desc[cur ^ 1], itx_n, per_entry, __builtin_amdgcn_readfirstlane(s_q[cur ^ 1]),
+                      wave, lane);
 
     // normalise; out through the wave's LDS area, so the stores are whole rows
     store_output<D>(p, o, halves_sum(l), prev.tok0, prev.qw, prev.n, prev.head, lane, io);
