@@ -35,7 +35,8 @@ struct WsHeader {
   int32_t part_tokens;              // decode partition size the plan chose for this call
   int32_t pad0[2];
   uint32_t zeros[16];               // 64 zero bytes: the source of K/V rows never loaded
-  int32_t pad1[32];
+  int32_t group_next[kMaxQueues];   // per-XCD queues of the decode kernel's group items
+  int32_t pad1[24];
 };
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte line");
 

@@ -418,21 +418,45 @@ template <int D>
 __global__ void __launch_bounds__(256)
 decode_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
-  const int n_grp = p.hdr->n_group * p.hkv;   // group items come first: every one is a full partition
-  const int n_items = n_grp + p.hdr->n_decode * p.hkv;
-  if (n_items == 0) return;   // no decode segment in this step: no queue traffic
+  const int n_group = p.hdr->n_group;
+  if (n_group + p.hdr->n_decode == 0) return;   // no decode segment in this step: no queue traffic
   const int64_t row_bytes = (int64_t)p.hkv * D * 2;
   const int64_t block_bytes = 2 * kBlock * row_bytes;
   const int P = wave_uniform(p.hdr->part_tokens);   // the plan's partition size
 
+  // Group items first, every one a full partition.  When the KV heads split
+  // evenly over the eight XCDs, the group items of head g go to the queue of
+  // XCD g mod 8 (workgroup b runs on XCD b mod 8), which its waves drain
+  // before they turn to the shared queue: the groups that share a partition
+  // then read its K/V of head g through one L2, so the partition comes from
+  // HBM about once instead of once per group.
+  const bool xcd_groups = p.hkv % kMaxQueues == 0;
+  const int xq = blockIdx.x % kMaxQueues;
+  const int hpq = p.hkv / kMaxQueues;                     // heads per XCD queue
+  const int n_grp = xcd_groups ? 0 : n_group * p.hkv;     // group items in the shared queue
+  const int n_items = n_grp + p.hdr->n_decode * p.hkv;
+  bool own = xcd_groups && n_group > 0;   // still taking from this XCD's group queue
   for (;;) {
     int it = 0;
-    if (lane == 0) it = atomicAdd(&p.hdr->decode_next, 1);
+    if (lane == 0) it = atomicAdd(own ? &p.hdr->group_next[xq] : &p.hdr->decode_next, 1);
     it = wave_uniform(__shfl(it, 0));
-    if (it >= n_items) break;
-    if (it < n_grp) {
-      const GroupItem gi = p.groups[it / p.hkv];
-      const int g = it % p.hkv;
+    int gix = -1, g = 0;   // a group item: its entry and head
+    if (own) {
+      if (it >= n_group * hpq) {
+        own = false;
+        continue;
+      }
+      gix = it / hpq;
+      g = xq + kMaxQueues * (it % hpq);
+    } else {
+      if (it >= n_items) break;
+      if (it < n_grp) {
+        gix = it / p.hkv;
+        g = it % p.hkv;
+      }
+    }
+    if (gix >= 0) {
+      const GroupItem gi = p.groups[gix];
       if (gi.nmem * p.group <= 16)
         group_item<D, 1>(p, P, gi, g, lane, row_bytes, block_bytes);
       else
@@ -441,7 +465,7 @@ decode_kernel(DecodeParams p) {
     }
     it -= n_grp;
     const int2 item = p.items[it / p.hkv];
-    const int g = it % p.hkv;
+    g = it % p.hkv;
     const int s = item.x;
     const int part = item.y;
     const int L = p.lens[s];

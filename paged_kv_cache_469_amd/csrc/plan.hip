@@ -594,7 +594,10 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
     p.hdr->part_tokens = P;
     p.hdr->decode_next = 0;
   }
-  if (threadIdx.x < kMaxQueues) p.hdr->prefill_next[threadIdx.x] = 0;
+  if (threadIdx.x < kMaxQueues) {
+    p.hdr->prefill_next[threadIdx.x] = 0;
+    p.hdr->group_next[threadIdx.x] = 0;
+  }
 }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
