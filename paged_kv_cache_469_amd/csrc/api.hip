@@ -117,7 +117,7 @@ Layout layout(int32_t num_seqs, int32_t num_tokens, int32_t hq, int32_t hkv, int
   l.part_ml = off;
   off = align256(off + (size_t)l.rows_cap * l.pmax * hq * sizeof(float2));
   l.part_o = off;
-  off = align256(off + (size_t)l.rows_cap * l.pmax * hq * head_dim * sizeof(float));
+  off = align256(off + (size_t)l.rows_cap * l.pmax * hq * head_dim * sizeof(uint16_t));
   l.total = off;
   return l;
 }
@@ -303,7 +303,7 @@ int attention_impl(const char* who, const void* q, const void* kv_cache,
   dp.cu = cu_seqlens_q;
   dp.lens = seq_lens;
   dp.out = static_cast<uint16_t*>(out);
-  dp.part_o = reinterpret_cast<float*>(ws + l.part_o);
+  dp.part_o = reinterpret_cast<uint16_t*>(ws + l.part_o);
   dp.part_ml = reinterpret_cast<float2*>(ws + l.part_ml);
   dp.hdr = hdr;
   dp.items = pp.decode_items;

@@ -285,6 +285,11 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
     if (kn2 >= key1) break;
   }
 
+  // Each row leaves normalised, o / l, in bf16: into the output when the
+  // item is the segment's only partition, else into the partition's partial
+  // row (its m and l beside it in fp32), which the merge weighs by l.  Partial
+  // rows in bf16 halve the bytes this kernel writes into the middle of its
+  // read stream, where a written byte costs several read bytes.
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     float l = l_run[c];
@@ -292,33 +297,22 @@ __device__ __forceinline__ void decode_rows(const DecodeParams& p, const int32_t
     l += __shfl_xor(l, 32);
     if (!rm.live[c]) continue;
     const int hq = rm.hq[c];
-    if (direct) {
-      const float inv = 1.f / l;
-      uint16_t* orow = p.out + ((int64_t)rm.qtok[c] * p.hq + hq) * D;
+    const float inv = l > 0.f ? 1.f / l : 0.f;   // l = 0: the row saw no key of the partition
+    const int64_t slot = ((int64_t)rm.prow[c] * p.pmax + part) * p.hq + hq;
+    uint16_t* orow = direct ? p.out + ((int64_t)rm.qtok[c] * p.hq + hq) * D : p.part_o + slot * D;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        uint32_t wv[NT / 2];
+    for (int rr = 0; rr < 4; ++rr) {
+      uint32_t wv[NT / 2];
 #pragma unroll
-        for (int t = 0; t < NT; t += 2) wv[t / 2] = pack_bf16(o[c][t][rr] * inv, o[c][t + 1][rr] * inv);
-        uint16_t* dst = orow + NT * (4 * j + rr);
-        if constexpr (NT == 8) {
-          *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-        } else {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
-        }
+      for (int t = 0; t < NT; t += 2) wv[t / 2] = pack_bf16(o[c][t][rr] * inv, o[c][t + 1][rr] * inv);
+      uint16_t* dst = orow + NT * (4 * j + rr);
+      if constexpr (NT == 8) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      } else {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
       }
-    } else {
-      const int64_t slot = ((int64_t)rm.prow[c] * p.pmax + part) * p.hq + hq;
-      float* prow = p.part_o + slot * D;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        float* dst = prow + NT * (4 * j + rr);
-#pragma unroll
-        for (int t = 0; t < NT; t += 4)
-          *reinterpret_cast<f32x4*>(dst + t) = f32x4{o[c][t][rr], o[c][t + 1][rr], o[c][t + 2][rr], o[c][t + 3][rr]};
-      }
-      if (j == 0) p.part_ml[slot] = make_float2(m_run[c], l);
     }
+    if (!direct && j == 0) p.part_ml[slot] = make_float2(m_run[c], l);
   }
 }
 
@@ -483,9 +477,10 @@ decode_kernel(DecodeParams p) {
 
 // Merge of the partitions of every multi-partition decode segment.  One wave
 // per (segment, query head), for each of the segment's new tokens; lanes
-// split d.  The weights exp2(m_p - max m) rescale each partition's sum and
-// output to the common maximum (a partition none of whose keys a token sees
-// has m_p = -inf and weight 0; partition 0 always holds key 0).  Lane i
+// split d.  Partition p left o_p / l_p (bf16) with m_p and l_p; the weights
+// l_p exp2(m_p - max m) bring every partition to the common maximum (a
+// partition none of whose keys a token sees has m_p = -inf and weight 0;
+// partition 0 always holds key 0), and the output is their weighted mean.  Lane i
 // holds the weight of partitions i, i + 64, ...; the partials' rows are read
 // eight partitions at a time, so their loads overlap instead of paying one
 // memory round trip per partition.
@@ -525,11 +520,12 @@ decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     for (int i0 = 0; i0 < nparts; i0 += 64) {
-      // weight of partition i0 + lane
+      // weight of partition i0 + lane: its share of the sum, l_p exp2(m_p - M)
+      // (its row holds o_p / l_p)
       float wl = 0.f;
       if (i0 + lane < nparts) {
-        const float mp = p.part_ml[base + (int64_t)(i0 + lane) * p.hq].x;
-        wl = mp == -INFINITY ? 0.f : exp2f(mp - mx);
+        const float2 ml = p.part_ml[base + (int64_t)(i0 + lane) * p.hq];
+        wl = ml.x == -INFINITY ? 0.f : ml.y * exp2f(ml.x - mx);
       }
       const int cnt = min(64, nparts - i0);
       for (int j0 = 0; j0 < cnt; j0 += kBatch) {
@@ -537,9 +533,14 @@ decode_reduce_kernel(DecodeParams p, int32_t num_seqs, int32_t num_tokens) {
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const int i = i0 + min(j0 + j, cnt - 1);   // past the end: a repeated row, weight 0 below
-          const float* src = p.part_o + (base + (int64_t)i * p.hq) * D + lane * PER;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) v[j][e] = src[e];
+          const uint16_t* src = p.part_o + (base + (int64_t)i * p.hq) * D + lane * PER;
+          if constexpr (PER == 2) {
+            const uint32_t w2 = *reinterpret_cast<const uint32_t*>(src);
+            v[j][0] = bf16_lo(w2);
+            v[j][1] = bf16_hi(w2);
+          } else {
+            v[j][0] = bf16_lo(*src);
+          }
         }
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {

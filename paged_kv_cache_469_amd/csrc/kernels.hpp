@@ -60,7 +60,7 @@ struct DecodeParams {
   const int32_t* cu;
   const int32_t* lens;
   uint16_t* out;
-  float* part_o;           // [rows, pmax, Hq, D]
+  uint16_t* part_o;        // [rows, pmax, Hq, D] bf16: each partition's o / l
   float2* part_ml;         // [rows, pmax, Hq]  (running max in log2 units, sum)
   const int32_t* seg_row;  // per segment: its first partial row (token 0), -1 if not decode
   WsHeader* hdr;
