@@ -37,6 +37,7 @@
 // outside the pool, arrive as zeros, so poison in unused pool memory never
 // reaches the products.
 #include "kernels.hpp"
+#include "matrix_phase.inc"
 
 namespace pkv {
 namespace {
@@ -286,6 +287,36 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2
   pipe_order<4 * G::NDT, 2, PKV_PV_LEAD, VALU>();
 }
 
+// The matrix phase at head size 128 as one fixed instruction stream (the
+// schedule comes from gen_matrix_phase.py): QK(t) and PV(t-1) back to back
+// with the operand reads three groups ahead and every wait counting only the
+// reads issued after the one it needs.  (The compiler's own schedule of the
+// two loops drains the reads at the end of QK and leaves several reads one
+// MFMA ahead.)  It runs at every step: at t = 0, P is zero and the V slot it
+// reads was cleared when the item started; at t = ntiles the scores of the
+// stale K slot are never used.  One asm statement on every path keeps the
+// accumulators in the same registers (alternatives on different paths make
+// the compiler copy them and spill).  ak and av hold the lane's offsets plus
+// the slot array's base; KB and VB are the K and V slot's offsets in it.
+static_assert(PKV_MAT_RING_FIRST == 240, "the clobber list names the schedule's ring registers");
+
+template <int KB, int VB>
+__device__ __forceinline__ void matrix_phase_128(f32x16 (&s)[2], f32x16 (&o)[4], const u32x4 (&q)[8],
+                                                 const u32x4 (&pr)[2][2], const uint32_t (&ak)[8],
+                                                 const uint32_t (&av)[4]) {
+  asm volatile(PKV_MAT_QKPV
+               : [s0] "=&v"(s[0]), [s1] "=&v"(s[1]), [o0] "+v"(o[0]), [o1] "+v"(o[1]), [o2] "+v"(o[2]),
+                 [o3] "+v"(o[3])
+               : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
+                 [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [p0] "v"(pr[0][0]), [p1] "v"(pr[0][1]),
+                 [p2] "v"(pr[1][0]), [p3] "v"(pr[1][1]), [k0] "v"(ak[0]), [k1] "v"(ak[1]), [k2] "v"(ak[2]),
+                 [k3] "v"(ak[3]), [k4] "v"(ak[4]), [k5] "v"(ak[5]), [k6] "v"(ak[6]), [k7] "v"(ak[7]),
+                 [v0] "v"(av[0]), [v1] "v"(av[1]), [v2] "v"(av[2]), [v3] "v"(av[3]), [kb] "n"(KB),
+                 [vb] "n"(VB)
+               : "memory", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249",
+                 "v250", "v251", "v252", "v253", "v254", "v255");
+}
+
 // Online softmax of one tile, in two parts so the matrix phase can take
 // the first:
 //   tile_max  the row maximum of the tile's scores (after dropping keys past
@@ -471,8 +502,12 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   // The partner wave of this SIMD runs its softmax meanwhile: this wave's
   // products go first when both have an instruction ready.
   __builtin_amdgcn_s_setprio(1);
-  if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
-  if (t > 0) pv<D>(o, pr, av, v_prev);
+  if constexpr (D == 128) {
+    matrix_phase_128<RK * Geo<D>::TILEB, RV * Geo<D>::TILEB>(sc, o, q, pr, ak, av);
+  } else {
+    if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
+    if (t > 0) pv<D>(o, pr, av, v_prev);
+  }
   __builtin_amdgcn_s_setprio(0);
   if (!group_b) {
     // after the products are issued, while the last of them run
@@ -628,24 +663,19 @@ template <int D>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillParams p) {
   using G = Geo<D>;
-  // The slots are aligned to their size, above the 1024 of the queries'
-  // area, so they are laid out first, at the bottom of the LDS: the matrix
-  // phase addresses them with a lane's offset in a register and the slot's
-  // base in the instruction's 16-bit offset field, with no address
-  // arithmetic between the operand reads.
-  __shared__ __attribute__((aligned(G::TILEB))) char k0_lds[G::TILEB];
-  __shared__ __attribute__((aligned(G::TILEB))) char k1_lds[G::TILEB];
-  __shared__ __attribute__((aligned(G::TILEB))) char k2_lds[G::TILEB];
-  __shared__ __attribute__((aligned(G::TILEB))) char v0_lds[G::TILEB];
-  __shared__ __attribute__((aligned(G::TILEB))) char v1_lds[G::TILEB];
+  // The five tile slots are one array (K slots 0-2, V slots 0-1), aligned
+  // to a slot's size: the matrix phase addresses a slot with a lane's offset
+  // in a register and the slot's place in the instruction's 16-bit offset
+  // field, with no address arithmetic between the operand reads.
+  __shared__ __attribute__((aligned(G::TILEB))) char kv_lds[5 * G::TILEB];   // K0 K1 K2 V0 V1
   // per wave: its queries on their way in, its output on its way out
   __shared__ __attribute__((aligned(1024))) char io_lds[kWaves][32 * G::ROWB];
   __shared__ PrefillItem s_desc[2];   // the current and the next item
   __shared__ int s_itx[2];
   __shared__ int s_q[2];              // the queues they came from
   __shared__ int32_t s_bt[2][kWindow];   // block-table windows of the current item
-  const Slots<D> sl = {{(PKV_LDS char*)k0_lds, (PKV_LDS char*)k1_lds, (PKV_LDS char*)k2_lds},
-                       {(PKV_LDS char*)v0_lds, (PKV_LDS char*)v1_lds}};
+  PKV_LDS char* const kv = (PKV_LDS char*)kv_lds;
+  const Slots<D> sl = {{kv, kv + G::TILEB, kv + 2 * G::TILEB}, {kv + 3 * G::TILEB, kv + 4 * G::TILEB}};
   PKV_LDS char* const io = (PKV_LDS char*)io_lds[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
 
   const int lane = threadIdx.x & 63;
@@ -672,10 +702,18 @@ prefill_kernel(PrefillParams p) {
       const int d = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
       av[dt] = rr * G::ROWB + 16 * v_chunk<D>(rr, d >> 3) + 2 * (d & 7);
     }
+    if constexpr (D == 128) {
+      // the asm matrix phase addresses a slot by its offset in kv_lds
+#pragma unroll
+      for (int i = 0; i < G::NSL; ++i) ak[i] += lds_addr(sl.k[0]);
+#pragma unroll
+      for (int dt = 0; dt < G::NDT; ++dt) av[dt] += lds_addr(sl.v[0]);
+    }
   }
 
-  const CopyOff<D> ck = copy_offsets<D>(false, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
-  const CopyOff<D> cv = copy_offsets<D>(true, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
+  // group A copies only K and group B only V: one set of lane offsets each
+  const CopyOff<D> ck = copy_offsets<D>(group_b, wave & 3, lane, (uint32_t)(p.hkv * D * 2));
+  const CopyOff<D>& cv = ck;
 
   // the first item: wave 4 asks for its index and reads its descriptor
   if (wave == kWaves / 2) {
@@ -741,8 +779,15 @@ prefill_kernel(PrefillParams p) {
       for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
 
     if (group_b) s_bt[0][64 * (wave - kWaves / 2) + lane] = bt_next;   // window 0
+    if constexpr (D == 128) {
+      // the first step's PV multiplies P = 0 by V slot 1: clear what the
+      // item before left there (a non-finite value would survive the zero)
+      PKV_LDS u32x4* const v1 = reinterpret_cast<PKV_LDS u32x4*>(sl.v[1]);
+      v1[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+      v1[threadIdx.x + 512] = u32x4{0u, 0u, 0u, 0u};
+    }
     copies_landed<0>();   // the copies of K/V and of the queries
-    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS
+    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS; V slot 1 cleared
     read_queries<D>(q, io, lane, p.q_sign);
     // asked for only now, so the wait for the copies above does not include it
     if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[cq], 1);
