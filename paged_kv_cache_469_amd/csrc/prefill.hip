@@ -170,25 +170,36 @@ __device__ __forceinline__ CopyOff<D> copy_offsets(bool vhalf, int wq, int lane,
   return o;
 }
 
+// What a wave's block copies of one item share: the address of its group's
+// half (K for group A, V for group B) of KV head g in block 0, the bytes
+// from one block to the next and of one key row, and the pool's block count
+// (capped at 2^31 - 1: every nonnegative 32-bit id below it is in the pool).
+struct CopyGeo {
+  uint64_t base;
+  uint32_t bstride, rbytes, nb;
+};
+
 // Copy this wave's block (id bid, first key key0) of a tile into LDS at
 // lds_dst.  Keys at or past kend (one past the item's last needed key) and
 // every key of a block outside the pool arrive as zeros; a block outside the
-// pool that holds needed keys sets bad.
+// pool that holds needed keys sets bad.  All of it is scalar arithmetic:
+// one unsigned compare checks the id, one 32 x 32 -> 64-bit product places
+// the block.
 template <int D>
-__device__ __forceinline__ void copy_block(const PrefillParams& p, int bid, int key0, int kend,
-                                           int g, bool vhalf, const CopyOff<D>& co,
-                                           uint32_t lds_dst, uint32_t& bad) {
-  const int nvalid = min(max(kend - key0, 0), kBlock);
-  const bool ok = bid >= 0 && (int64_t)bid < p.num_blocks;
-  if (nvalid > 0 && !ok) bad = 1;
-  const int64_t row_bytes = (int64_t)p.hkv * D * 2;
-  const uint64_t base = reinterpret_cast<uint64_t>(p.cache) +
-                        (ok ? (uint64_t)bid * 2 * kBlock * row_bytes : 0) +
-                        (vhalf ? kBlock * row_bytes : 0) + (uint64_t)g * D * 2;
+__device__ __forceinline__ void copy_block(const CopyGeo& cg, int bid, int key0, int kend,
+                                           const CopyOff<D>& co, uint32_t lds_dst, uint32_t& bad) {
+  const uint32_t ub = (uint32_t)bid;
+  const int nv = min(kend - key0, kBlock);   // keys of the block the item needs, if positive
+  const bool need = nv > 0;
+  const bool ok = ub < cg.nb;
+  if (need && !ok) bad = 1;
+  // a select, not a clamp: a clamp becomes a vector med3
+  const uint32_t records = need && ok ? (uint32_t)nv * cg.rbytes : 0u;
+  const uint64_t base = cg.base + (uint64_t)(ok ? ub : 0u) * cg.bstride;
   // every field is wave-uniform; readfirstlane keeps the descriptor in SGPRs
   const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
                     (uint32_t)__builtin_amdgcn_readfirstlane((int)((base >> 32) & 0xffffu)),
-                    (uint32_t)__builtin_amdgcn_readfirstlane(ok ? (int)(nvalid * row_bytes) : 0),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int)records),
                     (uint32_t)kRsrcWord3};
   // one asm block: copy i lands 1 KiB after copy i-1 (M0 steps by 0x400;
   // an M0 write needs one wait state before the copy that uses it)
@@ -394,6 +405,7 @@ struct Item {
   int nblk;    // ceil(L / 16): entries of the block table in use
   int L, n, h, g, head, qw, kmax, ntiles, kfull, kend, lim, qi, tok0;
   bool active;
+  CopyGeo cg;  // this wave's block copies
 };
 
 // Item itx (descriptor d, in LDS) as this wave sees it.
@@ -422,12 +434,17 @@ __device__ __forceinline__ Item<D> item_of(const PrefillParams& p, const Prefill
   it.nblk = (it.L + kBlock - 1) / kBlock;
   it.qi = it.qw + (lane & 31);
   it.lim = it.h + it.qi;
+  const uint32_t rbytes = (uint32_t)(p.hkv * D * 2);
+  it.cg.rbytes = rbytes;
+  it.cg.bstride = 2 * kBlock * rbytes;
+  it.cg.nb = (uint32_t)min(p.num_blocks, (int64_t)INT32_MAX);
+  it.cg.base = reinterpret_cast<uint64_t>(p.cache) + (wave >= kWaves / 2 ? (uint64_t)kBlock * rbytes : 0) +
+               (uint64_t)it.g * D * 2;
   return it;
 }
 
 // LDS slots: K of three tiles (tile j in slot j % 3) and V of two (slot
-// j % 2), as separate objects so the compiler can tell that a copy into one
-// slot never touches the slot being read.
+// j % 2).
 template <int D>
 struct Slots {
   PKV_LDS char* k[3];
@@ -511,9 +528,9 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   __builtin_amdgcn_s_setprio(0);
   if (!group_b) {
     // after the products are issued, while the last of them run
-    const int bk = 4 * (t + 2) + wq;   // block of K(t+2)
-    const int bid_k = __builtin_amdgcn_readfirstlane(bt[(bk / kWindow) & 1][bk % kWindow]);
-    copy_block<D>(p, bid_k, kKeys * (t + 2) + kBlock * wq, it.kmax, it.g, false, ck,
+    const uint32_t bk = 4 * (t + 2) + wq;   // block of K(t+2); window (bk / 256) % 2
+    const int bid_k = __builtin_amdgcn_readfirstlane((&bt[0][0])[bk & (2 * kWindow - 1)]);
+    copy_block<D>(it.cg, bid_k, kKeys * (t + 2) + kBlock * wq, it.kmax, ck,
                   lds_addr(sl.k[RP]) + wq * kBlockBytes, bad);
   }
   if (group_b) copies_landed<0>();   // V(t), copied during the step before
@@ -533,9 +550,9 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
       const int32_t* src = reinterpret_cast<const int32_t*>(p.items + min(nxt, n_items - 1) / per_entry);
       nxt_word = src[lane & 15];
     }
-    const int bv = 4 * (t + 1) + wq;   // block of V(t+1)
-    const int bid_v = __builtin_amdgcn_readfirstlane(bt[(bv / kWindow) & 1][bv % kWindow]);
-    copy_block<D>(p, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, it.g, true, cv,
+    const uint32_t bv = 4 * (t + 1) + wq;   // block of V(t+1)
+    const int bid_v = __builtin_amdgcn_readfirstlane((&bt[0][0])[bv & (2 * kWindow - 1)]);
+    copy_block<D>(it.cg, bid_v, kKeys * (t + 1) + kBlock * wq, it.kmax, cv,
                   lds_addr(v_prev) + wq * kBlockBytes, bad);
     if ((t & 63) == 1 && kWindow * w < it.nblk) bt_next = window_entry(it.bt_row, w, wave - kWaves / 2, lane, it.nblk);
   }
@@ -752,13 +769,11 @@ prefill_kernel(PrefillParams p) {
     if (group_b) bt_next = window_entry(nx.bt_row, 0, wave - kWaves / 2, lane, nx.nblk);
     copy_queries<D>(p, nx.tok0, nx.qw, nx.n, nx.head, lane, lds_addr(io));
     if (!group_b) {
-      copy_block<D>(p, bid0, kBlock * wq, nx.kmax, nx.g, false, ck,
-                    lds_addr(sl.k[0]) + wq * kBlock * G::ROWB, bad);
-      copy_block<D>(p, bid1, kKeys + kBlock * wq, nx.kmax, nx.g, false, ck,
-                    lds_addr(sl.k[1]) + wq * kBlock * G::ROWB, bad);
+      copy_block<D>(nx.cg, bid0, kBlock * wq, nx.kmax, ck, lds_addr(sl.k[0]) + wq * kBlock * G::ROWB, bad);
+      copy_block<D>(nx.cg, bid1, kKeys + kBlock * wq, nx.kmax, ck, lds_addr(sl.k[1]) + wq * kBlock * G::ROWB,
+                    bad);
     } else {
-      copy_block<D>(p, bid0, kBlock * wq, nx.kmax, nx.g, true, cv,
-                    lds_addr(sl.v[0]) + wq * kBlock * G::ROWB, bad);
+      copy_block<D>(nx.cg, bid0, kBlock * wq, nx.kmax, cv, lds_addr(sl.v[0]) + wq * kBlock * G::ROWB, bad);
     }
   };
   start_item(it, &s_desc[0]);
