@@ -210,13 +210,13 @@ __device__ __forceinline__ void copy_block(const CopyGeo& cg, int bid, int key0,
         "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
         "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
         :: "s"(lds_dst), "v"(co.g[0]), "v"(co.g[1]), "v"(co.g[2]), "v"(co.g[3]), "s"(rs)
-        : "memory", "scc");
+        : "memory", "scc", "m0");
   } else {
     static_assert(CopyOff<D>::NCH == 2, "copies per block");
     asm volatile(
         "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
         "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
-        :: "s"(lds_dst), "v"(co.g[0]), "v"(co.g[1]), "s"(rs) : "memory", "scc");
+        :: "s"(lds_dst), "v"(co.g[0]), "v"(co.g[1]), "s"(rs) : "memory", "scc", "m0");
   }
 }
 
@@ -615,7 +615,7 @@ __device__ __forceinline__ void copy_queries(const PrefillParams& p, int tok0, i
         "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %9, 0 offen lds"
         :: "s"(lds_dst), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]),
            "v"(off[5]), "v"(off[6]), "v"(off[7]), "s"(rs)
-        : "memory", "scc");
+        : "memory", "scc", "m0");
   } else {
     static_assert(NQ == 4, "copies per wave");
     asm volatile(
@@ -624,7 +624,7 @@ __device__ __forceinline__ void copy_queries(const PrefillParams& p, int tok0, i
         "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
         "s_add_u32 m0, m0, 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %5, 0 offen lds"
         :: "s"(lds_dst), "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(rs)
-        : "memory", "scc");
+        : "memory", "scc", "m0");
   }
 }
 
