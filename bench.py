@@ -317,7 +317,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 # traffic only while the sources still hash the same.
 KERNEL_SOURCES = {
     "decode_kernel": ["decode.hip", "common.hpp", "kernels.hpp"],
-    "prefill_kernel": ["prefill.hip", "common.hpp", "kernels.hpp"],
+    "prefill_kernel": ["prefill.hip", "matrix_phase.inc", "common.hpp", "kernels.hpp"],
 }
 
 
