@@ -511,10 +511,12 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   constexpr int RV = (S % 2) ^ 1;        // V slot of tiles t - 1 and t + 1
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
   const int wq = wave & 3;
-  // Matrix phase: QK(t) and PV(t-1), except that the first step has no P
-  // yet and the last one no tile to score (wave-uniform branches).  A tile
-  // the wave's queries do not see (past every key they see) has P = 0, and
-  // every slot read holds finite values, so its products change nothing.
+  // Matrix phase: QK(t) and PV(t-1).  At head size 128 both run at every
+  // step (the first step's P is zero over a cleared V slot, the last step's
+  // scores are not used); at 64 the first step skips PV and the last QK
+  // (wave-uniform branches).  A tile the wave's queries do not see (past
+  // every key they see) has P = 0, and every slot read holds finite values,
+  // so its products change nothing.
   PKV_LDS char* const v_prev = sl.v[RV];
   // The partner wave of this SIMD runs its softmax meanwhile: this wave's
   // products go first when both have an instruction ready.
