@@ -316,8 +316,10 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 # profiles/) records a hash of the kernel's sources; bench reports the
 # traffic only while the sources still hash the same.
 KERNEL_SOURCES = {
-    "decode_kernel": ["decode.hip", "common.hpp", "kernels.hpp"],
-    "prefill_kernel": ["prefill.hip", "matrix_phase.inc", "common.hpp", "kernels.hpp"],
+    # the plan decides the order of the work items, which sets how much of
+    # the K/V a kernel fetches from beyond L2
+    "decode_kernel": ["decode.hip", "plan.hip", "common.hpp", "kernels.hpp"],
+    "prefill_kernel": ["prefill.hip", "matrix_phase.inc", "plan.hip", "common.hpp", "kernels.hpp"],
 }
 
 

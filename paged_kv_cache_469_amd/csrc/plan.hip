@@ -15,11 +15,15 @@
 //             with the segment bounds and its first eight block ids
 //   n == 0 -> nothing
 // Both lists are ordered longest work first, so the dynamic queues hand out
-// the long items first and the short ones fill the tail: prefill items by
-// their number of 64-key tiles (a counting sort over 1024 cost buckets),
-// decode items by their keys (full partitions first, then the partial last
-// partitions of the segments by decreasing length, in 32-key buckets).  Segments whose
-// bounds are out of range are skipped and flagged.  The kernel also resets
+// the long items first and the short ones fill the tail.  Prefill items go
+// segment by segment, the segments by the number of 64-key tiles of their
+// costliest (last) query tile (a counting sort over 1024 cost buckets), a
+// segment's query tiles by decreasing cost: the workgroups of one XCD then
+// work on one segment at a time and read its K/V through their L2 (with
+// more than 1024 segments, items are sorted one by one by their own cost).
+// Decode items go by their keys (full partitions first, then the partial
+// last partitions of the segments by decreasing length, in 32-key buckets).
+// Segments whose bounds are out of range are skipped and flagged.  The kernel also resets
 // the status word and the dynamic-scheduling counters and writes the zero
 // line of the header, so the workspace needs no clearing between calls.
 #include "kernels.hpp"
@@ -469,10 +473,12 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
   if (dec_base > p.decode_cap) status |= 1u;
   __syncthreads();
   if (one_chunk && pre_total > 0) {   // pass 1b: the cost histogram, one wave per prefill segment
+    // segment-major: a segment's items go together, in the bucket of its
+    // costliest (last) query tile
     for (int k = wave; k < pl_count; k += 16) {
       const int n = pl_n[k], L = pl_len[k];
       const int np = (n + p.query_tile - 1) / p.query_tile;
-      for (int qt = lane; qt < np; qt += 64) atomicAdd(&hist[cost_key(n, L, qt, p.query_tile)], 1);
+      if (lane == 0) atomicAdd(&hist[cost_key(n, L, np - 1, p.query_tile)], np);
     }
     __syncthreads();
   } else if (pre_total > 0) {   // more than 1024 segments: one thread per segment
@@ -555,8 +561,11 @@ __global__ void __launch_bounds__(1024) plan_kernel(PlanParams p) {
       it.n = n;
 #pragma unroll
       for (int j = 0; j < 8; ++j) it.bid[j] = __shfl(bid, j);
+      int at0 = 0;
+      if (lane == 0) at0 = atomicAdd(&hist[cost_key(n, L, np - 1, p.query_tile)], np);
+      at0 = __shfl(at0, 0);
       for (int qt = lane; qt < np; qt += 64) {
-        const int at = atomicAdd(&hist[cost_key(n, L, qt, p.query_tile)], 1);
+        const int at = at0 + (np - 1 - qt);   // the segment's tiles by decreasing cost
         it.qt = qt;
         if (at < p.prefill_cap) p.prefill_items[at] = it;
       }
