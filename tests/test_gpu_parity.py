@@ -446,3 +446,34 @@ def test_full_spec_verify_8b():
     sample = np.random.default_rng(3).choice(wl.num_seqs, 8, replace=False)
     got, ref = _full_sampled(wl, sample, fill_others=True)
     check_close(got, ref, "spec_verify_8b full (8 sampled requests)")
+
+
+def _random_batch(seed):
+    """A seeded mixed batch: a head layout (G from 1 to 8, head size 64 or
+    128) and 1-12 segments, each a single-token decode, a few-token verify
+    (2-8 new tokens), an empty segment or a prompt chunk (9-259 new tokens),
+    over a history of 0-2999 cached tokens."""
+    rng = np.random.default_rng([469, 77, seed])
+    layouts = [(8, 8, 64), (16, 8, 128), (32, 8, 128), (32, 4, 64), (64, 8, 128), (6, 2, 128),
+               (32, 4, 128)]
+    hq, hkv, d = layouts[int(rng.integers(len(layouts)))]
+    segs = []
+    for _ in range(int(rng.integers(1, 13))):
+        kind = rng.choice(4, p=[0.5, 0.2, 0.05, 0.25])
+        n = [1, int(rng.integers(2, 9)), 0, int(rng.integers(9, 260))][kind]
+        segs.append((n, int(rng.integers(0, 3000)) + n))
+    if all(n == 0 for n, _ in segs):
+        segs[0] = (1, segs[0][1] + 1)
+    return hq, hkv, d, segs
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_batches(seed):
+    hq, hkv, d, segs = _random_batch(seed)
+    wl = _custom(hq, hkv, d, segs, cfg=60 + seed)
+    log(f"case random {seed}: heads {hq}/{hkv}, d {d}, (n, L) {segs}")
+    st = DeviceStep(wl, host_pool=True)
+    out = down_u16(st.attend())
+    assert np.array_equal(down_u16(st.pool), st.host)
+    ref = paged.attend(st.q_host, st.host, wl.block_tables, wl.cu_seqlens_q, wl.seq_lens, wl.scale)
+    check_close(out, ref, f"random batch {seed}")
