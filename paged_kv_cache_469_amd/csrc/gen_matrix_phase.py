@@ -10,6 +10,16 @@ four-register slots (fixed registers RING_BASE..), and every wait counts
 only the reads issued after the one it needs, so QK and PV run as one
 stream with no drain between them.
 
+Two scalar branches inside the stream skip the half of it that a step does
+not need: QK when %[qrem] (tiles left after this one) is zero, the last
+step, whose scores would go unused; PV when %[tt] (the step) is zero, the
+first step, which has no P yet.  The path without QK issues the first LEAD
+PV reads itself, in the order and into the slots the QK path issues them,
+so both paths reach the PV body with the same reads in flight; every path
+ends by waiting for all reads, so none lands in a ring register after the
+block.  The branches are wave-uniform and invisible to the compiler, so
+the accumulators stay in one set of registers on every path.
+
 Operands of the asm statement that uses these strings (prefill.hip):
   %[s0] %[s1]      S^T halves (f32x16, written)
   %[o0] .. %[o3]   O^T d tiles (f32x16, read-write)
@@ -18,6 +28,7 @@ Operands of the asm statement that uses these strings (prefill.hip):
   %[k0] .. %[k7]   lane offsets of the K operand of slab i (bytes)
   %[v0] .. %[v3]   lane offsets of the V operand of d tile i (bytes)
   %[kb] %[vb]      LDS byte address of the K and V slot (immediates)
+  %[qrem] %[tt]    tiles left after this step, and the step (scalars)
 
 Run from this folder: python gen_matrix_phase.py (the generated file is
 committed; the build does not run this).
@@ -72,21 +83,41 @@ def pv_groups():
     return out
 
 
-def schedule(groups):
+def run(groups, first, last, issued):
+    """MFMAs first .. last - 1, each after the wait for its own reads and
+    followed by the reads LEAD groups ahead; issued = groups whose reads are
+    already out.  Returns (lines, issued)."""
     lines = []
-    issued = 0
-    n = len(groups)
-    for g in range(min(LEAD, n)):
-        lines += groups[g][1](slot(g))
-        issued += 1
-    for g in range(n):
+    for g in range(first, last):
         after = sum(groups[j][0] for j in range(g + 1, issued))
         lines.append(f"s_waitcnt lgkmcnt({after})")
         lines.append(groups[g][2](slot(g)))
-        if issued < n:
+        if issued < len(groups):
             lines += groups[issued][1](slot(issued))
             issued += 1
-    return lines + TAIL_NOPS
+    return lines, issued
+
+
+def schedule(qk, pv):
+    groups = qk + pv
+    nq, n = len(qk), len(qk) + len(pv)
+    lines = ["s_cmp_eq_u32 %[qrem], 0", "s_cbranch_scc1 2f"]   # no QK: to 2
+    for g in range(LEAD):
+        lines += groups[g][1](slot(g))
+    body, issued = run(groups, 0, nq, LEAD)
+    lines += body
+    lines += ["s_cmp_eq_u32 %[tt], 0", "s_cbranch_scc1 4f",     # no PV: to the end
+              "s_branch 3f",
+              "2:",
+              "s_cmp_eq_u32 %[tt], 0", "s_cbranch_scc1 4f"]
+    # the PV reads the QK path issued during its last MFMAs
+    for g in range(nq, issued):
+        lines += groups[g][1](slot(g))
+    lines.append("3:")
+    body, issued = run(groups, nq, n, issued)
+    lines += body
+    # nothing in flight past the block (a path without PV leaves reads out)
+    return lines + ["4:", "s_waitcnt lgkmcnt(0)"] + TAIL_NOPS
 
 
 def cstr(lines):
@@ -104,7 +135,7 @@ def text():
         f"// Matrix phase of the prefill kernel at head size {D}: operand reads {LEAD} groups\n",
         f"// ahead in a ring of {RING} slots (v{RING_BASE}..v{RING_BASE + 4 * RING - 1}).\n",
         f"#define PKV_MAT_RING_FIRST {RING_BASE}\n",
-        f"#define PKV_MAT_QKPV {cstr(head + schedule(qk_groups() + pv_groups()))}\n",
+        f"#define PKV_MAT_QKPV {cstr(head + schedule(qk_groups(), pv_groups()))}\n",
     ])
 
 

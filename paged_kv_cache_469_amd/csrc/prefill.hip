@@ -303,18 +303,19 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2
 // with the operand reads three groups ahead and every wait counting only the
 // reads issued after the one it needs.  (The compiler's own schedule of the
 // two loops drains the reads at the end of QK and leaves several reads one
-// MFMA ahead.)  It runs at every step: at t = 0, P is zero and the V slot it
-// reads was cleared when the item started; at t = ntiles the scores of the
-// stale K slot are never used.  One asm statement on every path keeps the
-// accumulators in the same registers (alternatives on different paths make
-// the compiler copy them and spill).  ak and av hold the lane's offsets plus
+// MFMA ahead.)  Two scalar branches inside the stream skip PV at t = 0 (no
+// P yet: tt = t is zero) and QK at t = ntiles (no tile left to score: qrem =
+// ntiles - t is zero).  The branches are the stream's own, so one asm
+// statement serves every step and the accumulators stay in the same
+// registers (alternative statements on different paths make the compiler
+// copy them and spill).  ak and av hold the lane's offsets plus
 // the slot array's base; KB and VB are the K and V slot's offsets in it.
 static_assert(PKV_MAT_RING_FIRST == 240, "the clobber list names the schedule's ring registers");
 
 template <int KB, int VB>
 __device__ __forceinline__ void matrix_phase_128(f32x16 (&s)[2], f32x16 (&o)[4], const u32x4 (&q)[8],
                                                  const u32x4 (&pr)[2][2], const uint32_t (&ak)[8],
-                                                 const uint32_t (&av)[4]) {
+                                                 const uint32_t (&av)[4], int qrem, int tt) {
   asm volatile(PKV_MAT_QKPV
                : [s0] "=&v"(s[0]), [s1] "=&v"(s[1]), [o0] "+v"(o[0]), [o1] "+v"(o[1]), [o2] "+v"(o[2]),
                  [o3] "+v"(o[3])
@@ -323,8 +324,8 @@ __device__ __forceinline__ void matrix_phase_128(f32x16 (&s)[2], f32x16 (&o)[4],
                  [p2] "v"(pr[1][0]), [p3] "v"(pr[1][1]), [k0] "v"(ak[0]), [k1] "v"(ak[1]), [k2] "v"(ak[2]),
                  [k3] "v"(ak[3]), [k4] "v"(ak[4]), [k5] "v"(ak[5]), [k6] "v"(ak[6]), [k7] "v"(ak[7]),
                  [v0] "v"(av[0]), [v1] "v"(av[1]), [v2] "v"(av[2]), [v3] "v"(av[3]), [kb] "n"(KB),
-                 [vb] "n"(VB)
-               : "memory", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249",
+                 [vb] "n"(VB), [qrem] "s"(qrem), [tt] "s"(tt)
+               : "memory", "scc", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249",
                  "v250", "v251", "v252", "v253", "v254", "v255");
 }
 
@@ -511,18 +512,16 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   constexpr int RV = (S % 2) ^ 1;        // V slot of tiles t - 1 and t + 1
   constexpr uint32_t kBlockBytes = kBlock * Geo<D>::ROWB;   // LDS bytes of one block's rows
   const int wq = wave & 3;
-  // Matrix phase: QK(t) and PV(t-1).  At head size 128 both run at every
-  // step (the first step's P is zero over a cleared V slot, the last step's
-  // scores are not used); at 64 the first step skips PV and the last QK
-  // (wave-uniform branches).  A tile the wave's queries do not see (past
-  // every key they see) has P = 0, and every slot read holds finite values,
-  // so its products change nothing.
+  // Matrix phase: QK(t) and PV(t-1); the first step skips PV and the last
+  // QK (wave-uniform branches, at head size 128 inside the stream).  A tile
+  // the wave's queries do not see (past every key they see) has P = 0, and
+  // every slot read holds finite values, so its products change nothing.
   PKV_LDS char* const v_prev = sl.v[RV];
   // The partner wave of this SIMD runs its softmax meanwhile: this wave's
   // products go first when both have an instruction ready.
   __builtin_amdgcn_s_setprio(1);
   if constexpr (D == 128) {
-    matrix_phase_128<RK * Geo<D>::TILEB, RV * Geo<D>::TILEB>(sc, o, q, pr, ak, av);
+    matrix_phase_128<RK * Geo<D>::TILEB, RV * Geo<D>::TILEB>(sc, o, q, pr, ak, av, it.ntiles - t, t);
   } else {
     if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
     if (t > 0) pv<D>(o, pr, av, v_prev);
@@ -796,15 +795,8 @@ prefill_kernel(PrefillParams p) {
       for (int u = 0; u < 2; ++u) pr[kt][u] = u32x4{0u, 0u, 0u, 0u};
 
     if (group_b) s_bt[0][64 * (wave - kWaves / 2) + lane] = bt_next;   // window 0
-    if constexpr (D == 128) {
-      // the first step's PV multiplies P = 0 by V slot 1: clear what the
-      // item before left there (a non-finite value would survive the zero)
-      PKV_LDS u32x4* const v1 = reinterpret_cast<PKV_LDS u32x4*>(sl.v[1]);
-      v1[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
-      v1[threadIdx.x + 512] = u32x4{0u, 0u, 0u, 0u};
-    }
     copies_landed<0>();   // the copies of K/V and of the queries
-    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS; V slot 1 cleared
+    __syncthreads();   // K(0), K(1), V(0), window 0 in LDS
     read_queries<D>(q, io, lane, p.q_sign);
     // asked for only now, so the wait for the copies above does not include it
     if (wave == kWaves / 2 && lane == 0) nxt = atomicAdd(&p.hdr->prefill_next[cq], 1);

@@ -42,20 +42,39 @@ def _regs(tok):
     return set(range(int(m.group(1)), int(m.group(2)) + 1))
 
 
-def test_stream_replays_correctly():
-    g = _gen()
-    lines = _stream()
-    assert lines[0] == "s_waitcnt lgkmcnt(0)"
+def _replay(lines, g, no_qk, no_pv):
+    """Follows the stream with %[qrem] == 0 iff no_qk and %[tt] == 0 iff no_pv;
+    returns the QK and PV terms of the MFMAs it issues."""
+    labels = {ln[:-1]: i for i, ln in enumerate(lines) if re.fullmatch(r"\d+:", ln)}
+    zero = {"%[qrem]": no_qk, "%[tt]": no_pv}
     inflight = []      # reads issued and not known to have landed: (regs, what it loads)
     holds = {}         # register -> what the last landed-or-pending read put there
     pending = set()    # registers with a read in flight
     consumed = set()   # registers whose contents an issued MFMA has read
     qk_terms, pv_terms = [], []
     s_started = {}
-    read_no = 0
-    for ln in lines[1:]:
+    scc = None
+    pc, steps = 0, 0
+    while pc < len(lines):
+        steps += 1
+        assert steps < 10 * len(lines), "the branches loop"
+        ln = lines[pc]
+        pc += 1
         op = ln.split()[0]
-        if op == "s_waitcnt":
+        if op == "s_cmp_eq_u32":
+            reg, imm = [t.rstrip(",") for t in ln.split()[1:3]]
+            assert imm == "0" and reg in zero, ln
+            scc = zero[reg]
+        elif op in ("s_cbranch_scc1", "s_branch"):
+            target = ln.split()[1]
+            assert target.endswith("f") and target[:-1] in labels, ln
+            assert labels[target[:-1]] > pc - 1, "branches only go forward"
+            if op == "s_branch" or scc:
+                pc = labels[target[:-1]] + 1
+            scc = None if op == "s_cbranch_scc1" else scc
+        elif re.fullmatch(r"\d+:", op):
+            pass
+        elif op == "s_waitcnt":
             n = int(re.search(r"lgkmcnt\((\d+)\)", ln).group(1))
             while len(inflight) > n:
                 regs, _ = inflight.pop(0)
@@ -66,7 +85,7 @@ def test_stream_replays_correctly():
             # the slot's previous contents were used by an MFMA already issued
             for r in regs:
                 if r in holds:
-                    assert r in consumed, f"read {read_no} overwrites v{r} before its MFMA issued"
+                    assert r in consumed, f"a read overwrites v{r} before its MFMA issued"
             addr = re.search(r"%\[(\w+)\] offset:%\[(\w+)\]\+(\d+)", ln)
             what = (op, addr.group(1), addr.group(2), int(addr.group(3)))
             inflight.append((regs, what))
@@ -74,7 +93,6 @@ def test_stream_replays_correctly():
                 holds[r] = what
                 pending.add(r)
                 consumed.discard(r)
-            read_no += 1
         elif op == "v_mfma_f32_32x32x16_bf16":
             dst, a, b, c = [t.rstrip(",") for t in ln.split()[1:5]]
             regs = _regs(a)
@@ -111,8 +129,20 @@ def test_stream_replays_correctly():
         else:
             assert op == "s_nop", ln
     assert not inflight, "every read is waited for inside the block"
-    assert sorted(qk_terms) == [(kt, sl) for kt in range(2) for sl in range(g.NSL)]
-    assert sorted(pv_terms) == [(dt, kt, u) for dt in range(g.NDT) for kt in range(2) for u in range(2)]
+    return qk_terms, pv_terms
+
+
+def test_stream_replays_correctly():
+    g = _gen()
+    lines = _stream()
+    assert lines[0] == "s_waitcnt lgkmcnt(0)"
+    all_qk = [(kt, sl) for kt in range(2) for sl in range(g.NSL)]
+    all_pv = [(dt, kt, u) for dt in range(g.NDT) for kt in range(2) for u in range(2)]
+    for no_qk in (False, True):
+        for no_pv in (False, True):
+            qk_terms, pv_terms = _replay(lines, g, no_qk, no_pv)
+            assert sorted(qk_terms) == ([] if no_qk else all_qk), (no_qk, no_pv)
+            assert sorted(pv_terms) == ([] if no_pv else all_pv), (no_qk, no_pv)
 
 
 def test_offsets_fit_the_instruction_field():
