@@ -45,13 +45,10 @@ namespace {
 constexpr int kKeys = 64;           // keys per tile
 constexpr int kWaves = 8;
 constexpr float kLazyMax = 8.f;     // how far (log2 units) m may trail the true maximum
-// MFMAs by which the LDS operand reads of the matrix phase run ahead
-#ifndef PKV_QK_LEAD
-#define PKV_QK_LEAD 3
-#endif
-#ifndef PKV_PV_LEAD
-#define PKV_PV_LEAD 3
-#endif
+// MFMAs by which the LDS operand reads of the compiled matrix phase (head
+// size 64) run ahead
+constexpr int kQkLead = 3;
+constexpr int kPvLead = 3;
 
 template <int D>
 struct Geo {
@@ -261,7 +258,7 @@ __device__ __forceinline__ void qk(f32x16 (&s)[2], const u32x4 (&q)[Geo<D>::NSL]
       s[kt] = mfma32(k, q[sl], sl == 0 ? f32x16{} : s[kt]);
     }
   }
-  pipe_order<2 * G::NSL, 1, PKV_QK_LEAD, VALU>();
+  pipe_order<2 * G::NSL, 1, kQkLead, VALU>();
 }
 
 // Scale O by alpha in the lanes whose maximum moved (a divergent branch:
@@ -295,7 +292,7 @@ __device__ __forceinline__ void pv(f32x16 (&o)[Geo<D>::NDT], const u32x4 (&pr)[2
       }
     }
   }
-  pipe_order<4 * G::NDT, 2, PKV_PV_LEAD, VALU>();
+  pipe_order<4 * G::NDT, 2, kPvLead, VALU>();
 }
 
 // The matrix phase at head size 128 as one fixed instruction stream (the
@@ -521,7 +518,9 @@ __device__ __forceinline__ void tile_step(const PrefillParams& p, const Item<D>&
   // products go first when both have an instruction ready.
   __builtin_amdgcn_s_setprio(1);
   if constexpr (D == 128) {
-    matrix_phase_128<RK * Geo<D>::TILEB, RV * Geo<D>::TILEB>(sc, o, q, pr, ak, av, it.ntiles - t, t);
+    matrix_phase_128<RK * Geo<D>::TILEB, RV * Geo<D>::TILEB>(sc, o, q, pr, ak, av,
+                                                             __builtin_amdgcn_readfirstlane(it.ntiles - t),
+                                                             __builtin_amdgcn_readfirstlane(t));
   } else {
     if (t < it.ntiles) qk<D>(sc, q, ak, sl.k[RK]);
     if (t > 0) pv<D>(o, pr, av, v_prev);
@@ -699,9 +698,6 @@ prefill_kernel(PrefillParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool group_b = wave >= kWaves / 2;
-#ifdef PKV_AGPR_HINT
-  asm volatile("" ::: "a0");   // lets the register allocator place MFMA accumulators in AGPRs
-#endif
   const int per_entry = (p.hkv / p.num_queues) * p.head_chunks;
   const int queue = blockIdx.x % p.num_queues;
   const int n_items = p.hdr->n_prefill * per_entry;
